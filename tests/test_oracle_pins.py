@@ -1,0 +1,409 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the pages or mathematics fix:
+hand-computed worked examples (tests/golden), closed forms, invariants,
+brute force on tiny inputs, and sampling-error-bounded statistics.  Pages:
+  "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends" [ROT]
+  "SpinQuant (learned rotations + W4A4KV4)" record [SQ]
+  "QuaRot (rotation-based outlier removal, W4A4KV4)" record [QR]
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_hadamard_matches_hand_written_h8():
+    rows = _golden_lines("hadamard8.txt")
+    ref = np.array([[1 if c == "+" else -1 for c in r.split()] for r in rows])
+    assert np.array_equal(O.hadamard(8), ref)
+    assert np.array_equal(O.hadamard(2), np.array([[1, 1], [1, -1]]))
+    assert np.array_equal(O.hadamard(1), np.array([[1]]))
+
+
+@pytest.mark.parametrize("n", [2, 4, 16, 128, 512, 1024])
+def test_hadamard_entries_closed_form(n):
+    """Sylvester's H has h_ij = (-1)^popcount(i & j) (textbook closed form)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(O.hadamard(n), np.where(pc % 2 == 0, 1, -1))
+
+
+@pytest.mark.parametrize("n", [1, 2, 8, 128, 1024])
+def test_hadamard_orthogonal(n):
+    """H H^T = n I exactly, so Q = H / sqrt(n) is orthogonal ([ROT] invariance needs Q Q^T = I)."""
+    h = O.hadamard(n).astype(np.float64)
+    assert np.array_equal(h @ h.T, n * np.eye(n))
+    assert np.array_equal(h, h.T)
+
+
+@pytest.mark.parametrize("n", [2048, 4096, 16384])
+def test_hadamard_large_sampled_entries(n):
+    h = O.hadamard(n)
+    rng = np.random.default_rng(n)
+    ii = rng.integers(0, n, 2000)
+    jj = rng.integers(0, n, 2000)
+    want = [(-1) ** bin(int(a) & int(b)).count("1") for a, b in zip(ii, jj)]
+    assert np.array_equal(h[ii, jj], np.array(want))
+
+
+def test_hadamard_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        O.hadamard(12)
+
+
+# ---------------------------------------------------------------- rotation
+def test_fwht_worked_examples():
+    for ln in _golden_lines("worked_examples.txt"):
+        if not ln.startswith("fwht"):
+            continue
+        head, xs, zs = [p.strip() for p in ln.split("|")]
+        n = int(head.split()[1])
+        x = np.array([float(v) for v in xs.split()])[None, :]
+        z = np.array([float(v) for v in zs.split()])
+        assert x.shape[1] == n
+        assert np.array_equal(O.rotate(x, n)[0], z), ln
+
+
+def _butterfly(v):
+    """Independent recursive fast Walsh-Hadamard transform on Python ints/Fractions."""
+    n = len(v)
+    if n == 1:
+        return list(v)
+    a = _butterfly(v[: n // 2])
+    b = _butterfly(v[n // 2:])
+    return [p + q for p, q in zip(a, b)] + [p - q for p, q in zip(a, b)]
+
+
+@pytest.mark.parametrize("block", [2, 8, 32, 128])
+def test_rotate_equals_exact_butterfly(block):
+    """The dense float64 product equals an exact rational butterfly, bit for bit."""
+    x = WL.small_random(1, 3, 2 * block, outlier_cols=[1], mult=40.0)
+    z = O.rotate(x, block)
+    for r in range(3):
+        for b0 in range(0, 2 * block, block):
+            exact = _butterfly([Fraction(float(v)) for v in x[r, b0:b0 + block]])
+            assert [Fraction(float(v)) for v in z[r, b0:b0 + block]] == exact
+
+
+@pytest.mark.parametrize("block", [128, 4096])
+def test_invariance_xwT(block):
+    """[ROT] "A rotation changes nothing": X W^T = (XQ)(WQ)^T, to 1e-10 in float64."""
+    x = WL.qproj(M=256, with_w=False)["X"].astype(np.float64)
+    w = WL.small_random(2, 256, 4096, std=0.02).astype(np.float64)
+    ref = x @ w.T
+    rot = O.rotate_normalized(x, block) @ O.rotate_normalized(w, block).T
+    assert np.linalg.norm(ref - rot) / np.linalg.norm(ref) < 1e-10
+
+
+@pytest.mark.parametrize("block", [1, 128, 1024])
+def test_involution_and_parseval(block):
+    x = WL.small_random(3, 8, 2048, outlier_cols=[5], mult=30.0).astype(np.float64)
+    y = O.rotate_normalized(x, block)
+    assert np.allclose(O.rotate_normalized(y, block), x, rtol=0, atol=1e-12)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("n,j,m", [(128, 3, 50.0), (128, 77, -50.0), (4096, 1234, 30.0)])
+def test_outlier_spreads_evenly(n, j, m):
+    """[ROT] "A rotation changes nothing": an outlier M in channel j becomes
+    +-M/sqrt(n) in every channel, the sign being H's row j."""
+    x = np.zeros((1, n))
+    x[0, j] = m
+    y = O.rotate_normalized(x, n)[0]
+    pc = np.array([bin(j & i).count("1") for i in range(n)])
+    assert np.allclose(y, m / math.sqrt(n) * np.where(pc % 2 == 0, 1, -1), rtol=1e-15, atol=0)
+    q = O.quant_sym_rows(O.rotate(x, n), n)
+    assert np.array_equal(q["codes"][0], 7 * np.sign(m) * np.where(pc % 2 == 0, 1, -1))
+    # s = max|y| / 7 = |M| / (7 sqrt(n))
+    assert q["scale"][0] == np.float32(abs(m)) / np.float32(7 * math.sqrt(n))
+
+
+def test_constant_row_concentrates():
+    """A constant row c.1 rotates to c*b at index 0 of every block, zeros elsewhere."""
+    x = np.full((1, 512), -3.0)
+    z = O.rotate(x, 128)[0].reshape(4, 128)
+    assert np.all(z[:, 0] == -3.0 * 128) and np.all(z[:, 1:] == 0)
+    q = O.quant_sym_rows(z.reshape(1, -1), 128)["codes"].reshape(4, 128)
+    assert np.all(q[:, 0] == -7) and np.all(q[:, 1:] == 0)
+
+
+def test_rotation_of_fp16_is_exact_integer_multiple():
+    """fp16 inputs: z * 2^24 is an integer below 2^53 (the rotation is exact)."""
+    x = WL.qproj(M=64, with_w=False)["X"]
+    z = O.rotate(x, 4096) * 2.0 ** 24
+    assert np.all(z == np.rint(z)) and np.abs(z).max() < 2.0 ** 53
+
+
+# ---------------------------------------------------------------- quantizers
+def test_quant_worked_examples():
+    for ln in _golden_lines("worked_examples.txt"):
+        kind = ln.split("|")[0].strip()
+        if kind == "sym":
+            _, zs, qs, ss, bs = [p.strip() for p in ln.split("|")]
+            z = np.array([[float(v) for v in zs.split()]])
+            d = O.quant_sym_rows(z, 1)
+            assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
+            assert d["scale"][0] == np.float32(float(ss)), ln
+            assert O.pack_nibbles(d["codes"])[0].tolist() == [int(b, 16) for b in bs.split()], ln
+        elif kind == "asym":
+            _, zs, qs, ss, zps = [p.strip() for p in ln.split("|")]
+            z = np.array([[float(v) for v in zs.split()]])
+            d = O.quant_asym_groups(z, 1, group=z.shape[1])
+            assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
+            assert d["scale"][0, 0] == np.float32(float(ss)), ln
+            assert d["zp"][0, 0] == int(zps), ln
+
+
+def _brute_code(t, lo, hi):
+    """Nearest integer in [lo, hi] to t, ties to the even one (exhaustive search)."""
+    best = None
+    for q in range(lo, hi + 1):
+        key = (abs(Fraction(t) - q), q % 2)
+        if best is None or key < best[0]:
+            best = (key, q)
+    return best[1]
+
+
+def test_sym_codes_brute_force():
+    z = O.rotate(WL.small_random(4, 6, 256, outlier_cols=[9], mult=50.0), 128)
+    d = O.quant_sym_rows(z, 128)
+    for r in range(6):
+        for k in range(256):
+            assert d["codes"][r, k] == _brute_code(d["t"][r, k], -7, 7)
+
+
+def test_asym_levels_brute_force():
+    z = O.rotate(WL.small_random(5, 4, 256, outlier_cols=[2], mult=20.0), 128)
+    d = O.quant_asym_groups(z, 128)
+    for r in range(4):
+        for g in range(2):
+            zp = int(d["zp"][r, g])
+            assert zp == _brute_code(d["t_zp"][r, g], 0, 15)
+            for k in range(128):
+                lvl = _brute_code(d["t"][r, g * 128 + k], -100, 100)
+                assert d["codes"][r, g * 128 + k] == min(max(lvl + zp, 0), 15)
+
+
+@pytest.mark.parametrize("block", [128, 4096])
+def test_sym_quant_invariants(block):
+    x = WL.qproj(M=32, with_w=False)["X"]
+    z = O.rotate(x, block)
+    d = O.quant_sym_rows(z, block)
+    q, s = d["codes"].astype(np.int64), d["scale"].astype(np.float64)
+    y = z / math.sqrt(block)
+    assert q.min() >= -7 and q.max() <= 7
+    # no clipping: every element within half a step (fp32 slack on the scale)
+    assert np.all(np.abs(y - q * s[:, None]) <= 0.5 * s[:, None] * (1 + 1e-5))
+    # the largest element lands on +-7 with its own sign
+    am = np.argmax(np.abs(z), axis=1)
+    assert np.array_equal(q[np.arange(32), am], 7 * np.sign(z[np.arange(32), am]))
+    # scale ~ max|y| / 7 to fp32 accuracy
+    assert np.allclose(s, np.abs(y).max(axis=1) / 7, rtol=3e-7, atol=0)
+    # odd symmetry and power-of-two scale invariance
+    dn = O.quant_sym_rows(-z, block)
+    assert np.array_equal(dn["codes"], -d["codes"])
+    d2 = O.quant_sym_rows(z * 8, block)
+    assert np.array_equal(d2["codes"], d["codes"]) and np.array_equal(d2["scale"], d["scale"] * 8)
+    # monotone along each row
+    for r in range(4):
+        o = np.argsort(z[r], kind="stable")
+        assert np.all(np.diff(q[r, o]) >= 0)
+
+
+def test_asym_quant_invariants():
+    x = WL.gateup(M=16, with_w=False)["X"]
+    z = O.rotate(x, 128)
+    d = O.quant_asym_groups(z, 128)
+    q = d["codes"].astype(np.int64).reshape(16, 64, 128)
+    zp = d["zp"].astype(np.int64)
+    s = d["scale"].astype(np.float64)
+    y = (z / math.sqrt(128)).reshape(16, 64, 128)
+    assert q.min() >= 0 and q.max() <= 15 and zp.max() <= 15
+    yh = (q - zp[:, :, None]) * s[:, :, None]
+    assert np.all(np.abs(y - yh) <= 0.5 * s[:, :, None] * (1 + 1e-5))
+    # the group minimum (when negative) maps to code 0 exactly
+    mn = y.min(axis=2)
+    idx = np.argmin(y, axis=2)
+    got = np.take_along_axis(q, idx[:, :, None], axis=2)[:, :, 0]
+    assert np.all(got[mn < 0] == 0)
+
+
+def test_zero_rows_and_groups():
+    z = np.zeros((2, 256))
+    d = O.quant_sym_rows(z, 128)
+    assert np.all(d["codes"] == 0) and np.all(d["scale"] == 0)
+    a = O.quant_asym_groups(z, 128)
+    assert np.all(a["codes"] == 0) and np.all(a["scale"] == 0) and np.all(a["zp"] == 0)
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_all_nibble_pairs():
+    lo, hi = np.meshgrid(np.arange(16), np.arange(16))            # lo varies fastest
+    q = np.stack([lo.ravel(), hi.ravel()], axis=1)
+    p = O.pack_nibbles(q)[:, 0]
+    assert np.array_equal(p, np.arange(256, dtype=np.uint8))      # lo + 16 hi enumerates 0..255
+    assert np.array_equal(O.unpack_nibbles(p[:, None], signed=False), q)
+    s = np.array([[-7, 7], [-1, -1], [7, -7], [0, -3]])
+    assert O.pack_nibbles(s)[:, 0].tolist() == [0x79, 0xFF, 0x97, 0xD0]
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(s), signed=True), s)
+
+
+# ---------------------------------------------------------------- integer GEMM and epilogues
+def test_int_gemm_brute_force():
+    rng = np.random.default_rng(9)
+    a = rng.integers(-7, 8, (5, 256))
+    b = rng.integers(-7, 8, (6, 256))
+    got = O.int_gemm(a, b)
+    for m in range(5):
+        for n in range(6):
+            assert got[m, n] == sum(int(a[m, k]) * int(b[n, k]) for k in range(256))
+    big = np.full((1, 14336), -7)
+    assert O.int_gemm(big, big)[0, 0] == 49 * 14336
+
+
+def test_epilogue_closed_forms():
+    acc = np.array([[3, -5], [0, 702464]])
+    ones = np.ones(2, np.float32)
+    assert np.array_equal(O.epilogue_sym_f32(acc, ones, ones), acc.astype(np.float32))
+    sx = np.array([0.5, 2.0], np.float32)
+    sw = np.array([0.25, 4.0], np.float32)
+    want = np.array([[0.375, -10.0], [0.0, 702464.0 * 8]], np.float32)
+    assert np.array_equal(O.epilogue_sym_f32(acc, sx, sw), want)
+
+
+def test_asym_gemm_brute_force():
+    rng = np.random.default_rng(10)
+    M, N, K = 3, 4, 256
+    u = rng.integers(0, 16, (M, K))
+    zp = rng.integers(0, 16, (M, K // 128))
+    qw = rng.integers(-7, 8, (N, K))
+    sx = rng.random((M, K // 128)).astype(np.float32)
+    sw = rng.random(N).astype(np.float32)
+    got = O.gemm_asym_f64(u, zp, sx, qw, sw)
+    gs = O.group_sums(qw)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for g in range(K // 128):
+                dot = sum(int(u[m, k]) * int(qw[n, k]) for k in range(g * 128, g * 128 + 128))
+                tot += Fraction(float(sx[m, g])) * (dot - int(zp[m, g]) * int(gs[n, g]))
+            assert abs(Fraction(float(got[m, n])) - tot * Fraction(float(sw[n]))) <= abs(tot) * Fraction(1, 2 ** 50)
+
+
+def test_linear_unit_scale_route():
+    """With every scale 1 the symmetric epilogue returns the integer product itself."""
+    rng = np.random.default_rng(11)
+    qa = rng.integers(-7, 8, (4, 128))
+    qb = rng.integers(-7, 8, (3, 128))
+    acc = O.int_gemm(qa, qb)
+    y = O.epilogue_sym_f32(acc, np.ones(4, np.float32), np.ones(3, np.float32))
+    assert np.array_equal(y, (qa @ qb.T).astype(np.float32))
+
+
+# ---------------------------------------------------------------- statistics
+def _mixture_kurtosis(var):
+    """Pearson kurtosis of a zero-mean Gaussian scale mixture with per-element variances `var`."""
+    var = np.asarray(var, np.float64)
+    return 3.0 * np.mean(var ** 2) / np.mean(var) ** 2
+
+
+def test_kurtosis_gaussian_is_three():
+    v = np.random.default_rng(12).standard_normal(4_000_000)
+    assert abs(O.kurtosis(v) - 3.0) < 4 * math.sqrt(24 / v.size)
+
+
+def test_kurtosis_qproj_before_and_after():
+    """[ROT] "A rotation changes nothing": heavy tails before, near 3 after a full-width rotation."""
+    d = WL.qproj(M=2048, with_w=False)
+    x = d["X"].astype(np.float64)
+    var_cols = np.ones(4096)
+    var_cols[d["outlier_cols"]] = 30.0 ** 2
+    before = _mixture_kurtosis(var_cols)
+    assert abs(O.kurtosis(x) / before - 1) < 0.10          # ~2.5% sampling s.d. from 16k outlier draws
+    full = O.kurtosis(O.rotate_normalized(x, 4096))
+    assert abs(full - 3.0) < 0.05
+    blk = O.kurtosis(O.rotate_normalized(x, 128))
+    assert abs(blk / _mixture_kurtosis(var_cols.reshape(32, 128).mean(axis=1)) - 1) < 0.03
+
+
+def test_kurtosis_downproj_blocks():
+    """Token-varying spikes: per-128-block variance is (127 + 40^2)/128 where the spike sits, else 1."""
+    d = WL.downproj(M=1024, with_w=False)
+    y = O.rotate_normalized(d["X"], 128)
+    nb = 14336 // 128
+    var_blocks = np.concatenate([np.full(nb - 1, 1.0), [(127 + 1600.0) / 128]])
+    assert abs(O.kurtosis(y) / _mixture_kurtosis(var_blocks) - 1) < 0.03
+
+
+def test_kurtosis_kv_heads():
+    d = WL.kv(B=1, H=4, S=1024)
+    y = O.rotate_normalized(d["KV"].reshape(-1, 128), 128)
+    assert abs(O.kurtosis(y) - 3.0) < 0.05
+    assert O.kurtosis(d["KV"]) > 20
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "qproj", "downproj"])
+def test_rotation_lowers_int4_product_error(cfg):
+    """[ROT] "What it buys in 4 bits": INT4 per-token / per-channel product
+    error is lower with the rotation than without (direction only)."""
+    if cfg == "tiny":
+        d = WL.tiny()
+        x, w = d["X"], d["W"]
+        blocks = [128]
+    elif cfg == "qproj":
+        d = WL.qproj(M=128)
+        x, w = d["X"], d["W"][:512]
+        blocks = [128, 4096]
+    else:
+        d = WL.downproj(M=128)
+        x, w = d["X"], d["W"][:256]
+        blocks = [128]
+    px = O.quant_sym_rows(x.astype(np.float64), 1)
+    pw = O.quant_sym_rows(w.astype(np.float64), 1)
+    e_plain = O.product_error(x, w, O.dequant_sym_rows(px["codes"], px["scale"]),
+                              O.dequant_sym_rows(pw["codes"], pw["scale"]))
+    for b in blocks:
+        r = O.w4a4_linear(x, w, b)
+        e_rot = O.product_error(x, w, O.dequant_sym_rows(r["act"]["codes"], r["act"]["scale"]),
+                                O.dequant_sym_rows(r["wq"]["codes"], r["wq"]["scale"]))
+        assert e_rot < e_plain, (b, e_rot, e_plain)
+        # the float64 product of the rotated, dequantized operands is the same Y as the oracle's
+        ref = O.epilogue_sym_f64(r["acc"], r["act"]["scale"], r["wq"]["scale"])
+        assert np.allclose(r["y"], ref, rtol=1e-12, atol=0)
+    assert O.outlier_ratio(O.rotate_normalized(x, blocks[-1])) < O.outlier_ratio(x)
+
+
+def test_asym_linear_matches_group_products():
+    d = WL.gateup(M=8, N=64)
+    r = O.w4a4_linear(d["X"], d["W"], 128, mode="asym")
+    a, wq = r["act"], r["wq"]
+    Ag = O.int_gemm_groups(a["codes"], a["zp"], wq["codes"])
+    y = (Ag * a["scale"].astype(np.float64)[:, None, :]).sum(axis=2) * wq["scale"].astype(np.float64)[None, :]
+    assert np.allclose(r["y"], y, rtol=1e-12, atol=1e-12)
+    xq = O.dequant_asym_groups(a["codes"], a["scale"], a["zp"])
+    wh = O.dequant_sym_rows(wq["codes"], wq["scale"])
+    assert np.allclose(r["y"], xq @ wh.T, rtol=1e-10, atol=1e-10)
+
+
+def test_kv_oracle_shapes_and_dequant():
+    d = WL.kv(B=1, H=2, S=16)
+    r = O.kv_rotate_quant(d["KV"], 128)
+    assert r["packed"].shape == (1, 2, 16, 64) and r["scale"].shape == (1, 2, 16)
+    y = O.rotate_normalized(d["KV"].reshape(-1, 128), 128)
+    yh = O.dequant_asym_groups(r["codes"], r["scale"].reshape(-1, 1), r["zp"].reshape(-1, 1))
+    assert np.all(np.abs(y - yh) <= 0.5 * r["scale"].reshape(-1, 1) * (1 + 1e-5))
