@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A4 hot path on one MI355X.
+
+Workload: the LLaMA-2-7B q_proj linear layer, X 2048x4096 fp16 (8 fixed
+outlier channels x30), W 4096x4096 fp16 ~N(0, 0.02), 128-wide Hadamard
+blocks (--had full: one 4096-point Hadamard), symmetric INT4 per token and
+per output channel.  Synthetic, seeded inputs from `workloads`.
+
+One step = one pass of the whole path over one batch:
+    quant_weight_offline(W)  -> rotate_quant_act(X)  -> w4a4_gemm
+Inputs sit in HBM before the timed region; 8 copies of the inputs and
+outputs are cycled so that a step never finds its operands in the 256 MiB
+last-level cache.  Every kernel is bracketed by HIP events on the stream it
+runs on, so the per-kernel averages come from the timed steps themselves.
+
+Prints one JSON line; value = 2*M*N*K / step time (TOPS of the whole step).
+`--suite` instead prints one line per kernel and configuration (cold and
+warm timings of every entry point, with rooflines).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+NSETS = 8
+
+
+def src_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "rotation_w4a4_quantization_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_traffic(kernel_key: str, src: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_hash:\s*(\w+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != src:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(reps: int = 3) -> dict:
+    """The CPU oracle on the same q_proj step, timed on this host's cores."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as WL
+    from threadpoolctl import threadpool_info
+
+    d = WL.qproj()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        wq = O.quant_weight_offline(d["W"], 128)
+        a = O.rotate_quant_act(d["X"], 128, "sym")
+        acc = O.int_gemm(a["codes"], wq["codes"])
+        O.epilogue_sym_f32(acc, a["scale"], wq["scale"])
+    dt = (time.perf_counter() - t0) / reps
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    M, N, K = 2048, 4096, 4096
+    return {"value": round(2 * M * N * K / dt / 1e12, 5), "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"full q_proj step (weight rotate+quant, activation rotate+quant, exact integer "
+                      f"GEMM, fp32 epilogue) at M=2048 N=K=4096, mean of {reps} runs, "
+                      f"{dt:.3f} s per step, numpy float64 + BLAS"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--had", choices=["128", "full"], default="128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this path has no multi-GPU mode; rows shard with no communication.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rotation_w4a4_quantization_amd as R
+    from rotation_w4a4_quantization_amd import _lib
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.suite:
+        from bench_suite import run_suite   # noqa: E402  (kept beside bench.py)
+        run_suite()
+        return 0
+
+    dev = torch.device("cuda:0")
+    M, N, K = 2048, 4096, 4096
+    block = 128 if args.had == "128" else K
+    hb = _lib.W4A4_HAD_128 if block == 128 else _lib.W4A4_HAD_FULL
+    d = WL.qproj(M=M)
+    X = torch.from_numpy(d["X"]).to(dev)
+    W = torch.from_numpy(d["W"]).to(dev)
+    sets = []
+    for _ in range(NSETS):
+        sets.append(dict(
+            x=X.clone(), w=W.clone(),
+            xc=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            xs=torch.empty((M,), dtype=torch.float32, device=dev),
+            wc=torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+            ws=torch.empty((N,), dtype=torch.float32, device=dev),
+            wg=torch.empty((N, K // 128), dtype=torch.int32, device=dev),
+            y=torch.empty((M, N), dtype=torch.float32, device=dev)))
+    del X, W
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    lib = _lib.load()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.quant_weight_offline(s["w"].data_ptr(), N, K, K, hb, s["wc"].data_ptr(),
+                                      s["ws"].data_ptr(), s["wg"].data_ptr(), sp)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.rotate_quant_act(s["x"].data_ptr(), M, K, K, hb, _lib.W4A4_ACT_SYM_TOKEN,
+                                   s["xc"].data_ptr(), s["xs"].data_ptr(), None, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        st |= lib.w4a4_gemm(s["xc"].data_ptr(), s["xs"].data_ptr(), None, _lib.W4A4_ACT_SYM_TOKEN,
+                            s["wc"].data_ptr(), s["ws"].data_ptr(), None, M, N, K, s["y"].data_ptr(),
+                            N, sp)
+        if ev is not None:
+            ev[3].record(stream)
+        if st:
+            raise RuntimeError(f"W4A4 call failed: {_lib.last_error()}")
+
+    for i in range(args.warmup):
+        step(sets[i % NSETS])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % NSETS], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kt = {"quant_weight_offline": 0.0, "rotate_quant_act": 0.0, "w4a4_gemm": 0.0}
+    for e in evs:
+        kt["quant_weight_offline"] += e[0].elapsed_time(e[1])
+        kt["rotate_quant_act"] += e[1].elapsed_time(e[2])
+        kt["w4a4_gemm"] += e[2].elapsed_time(e[3])
+    kt = {k: v / args.steps for k, v in kt.items()}      # ms per launch
+    ops = 2.0 * M * N * K
+    gemm_tops = ops / (kt["w4a4_gemm"] * 1e-3) / 1e12
+    act_bytes = 2 * M * K + M * K // 2 + 4 * M
+    w_bytes = 2 * N * K + N * K // 2 + 4 * N + 4 * N * (K // 128)
+    act_gbs = act_bytes / (kt["rotate_quant_act"] * 1e-3) / 1e9
+    w_gbs = w_bytes / (kt["quant_weight_offline"] * 1e-3) / 1e9
+
+    traffic = profile_traffic(f"w4a4_gemm_qproj_had{args.had}", src_hash("gemm.hip", "common.h"))
+    out = {
+        "metric": "W4A4 GEMM TOPS (frac INT8 MFMA peak) + rotate+quant GB/s, M×4096×4096",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes (int8 MFMA, int32 acc), fp32 transform/scales",
+        "data": "synthetic (seeded N(0,1) activations with 8 outlier channels x30, N(0,0.02) weights)",
+        "config": {"workload": f"LLaMA-2-7B q_proj W4A4 linear: M=2048, N=4096, K=4096, "
+                               f"Hadamard block {block}, symmetric INT4 per token / per channel",
+                   "M": M, "N": N, "K": K, "had_block": block},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic, "kernel": "w4a4_gemm (gemm_tile_kernel<sym>)",
+                     "per_launch_ops": ops, "avg_launch_ms": round(kt["w4a4_gemm"], 5)},
+        "kernels": {
+            "w4a4_gemm": {"avg_ms": round(kt["w4a4_gemm"], 5), "TOPS": round(gemm_tops, 1),
+                          "frac_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4)},
+            "rotate_quant_act": {"avg_ms": round(kt["rotate_quant_act"], 5), "GB/s": round(act_gbs, 1),
+                                 "frac_hbm_peak": round(act_gbs / HBM_PEAK_GBS, 4),
+                                 "bytes": act_bytes},
+            "quant_weight_offline": {"avg_ms": round(kt["quant_weight_offline"], 5),
+                                     "GB/s": round(w_gbs, 1),
+                                     "frac_hbm_peak": round(w_gbs / HBM_PEAK_GBS, 4), "bytes": w_bytes},
+        },
+        "event_ms_per_step": round(sum(kt.values()), 5),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * w4a4.h - C ABI of the MI355X (gfx950) W4A4 rotate / quantize / GEMM library.
+ *
+ * The method: a linear layer Y = X W^T is unchanged when X and W are both
+ * multiplied by the same orthogonal Q, so X Q and W Q are quantized instead
+ * of X and W; with Q a normalized Hadamard matrix an outlier channel is
+ * spread evenly over all channels and 4-bit activations become usable.
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   sections "A rotation changes nothing, and that is the point" (invariance,
+ *   Q = H / sqrt(n)), "What it buys in 4 bits" (INT4, one scale per token and
+ *   one per output channel), "Where the rotations go" (weights rotated
+ *   offline, activations rotated online by a fast Hadamard transform fused
+ *   with their quantization), "Gotchas" (128-wide blocks vs full width).
+ *   Page "SpinQuant (learned rotations + W4A4KV4)", field "Activation scheme"
+ *   (per-group asymmetric INT4 for activations and KV cache).
+ *   Page "QuaRot (rotation-based outlier removal, W4A4KV4)", field
+ *   "Activation scheme" (the KV cache is rotated too).
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library allocates no device memory and keeps no state besides its code
+ *    objects and a per-device architecture check.
+ *  - Every call is asynchronous and ordered on `stream` (a hipStream_t;
+ *    NULL means the null stream).  Buffers must stay alive until the stream
+ *    work completes.  Outputs must not alias inputs.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is launched, outputs are untouched, the status says
+ *    why and w4a4_last_error() holds a message.  A failed launch returns
+ *    W4A4_ERR_DEVICE.  Faults during execution surface at the caller's next
+ *    synchronization.
+ *  - M == 0 (or B*H*S == 0) returns W4A4_OK and enqueues nothing once the
+ *    modes and sizes are valid; pointers are not checked then (may be NULL).
+ *  - Matrices are row-major with K contiguous; fp16 inputs are raw IEEE
+ *    binary16 bit patterns (uint16_t).  NaN / Inf inputs are outside the
+ *    contract: the call does not crash, the values it writes are unspecified.
+ *  - Every pointer must be 16-byte aligned; row strides of fp16 inputs must
+ *    be multiples of 8 elements (W4A4_ERR_ALIGN otherwise).
+ *
+ * Hadamard (reading of the pages): the Sylvester matrix in natural order,
+ * H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], no random signs, applied to
+ * contiguous aligned blocks of `had_block` elements of every row along K
+ * (had_block = 128), or to the whole row (had_block = W4A4_HAD_FULL, K a
+ * power of two, 128 <= K <= 16384).  X and W must be rotated with the same
+ * had_block; the codes do not record it.
+ *
+ * Codes (reading): two 4-bit codes per byte, even K index in bits 3:0, odd
+ * index in bits 7:4; rows contiguous, K/2 bytes per row.  Symmetric codes
+ * are 4-bit two's complement in [-7, 7]; asymmetric codes are unsigned
+ * in [0, 15].  Rounding is to nearest, ties to even.
+ *
+ * Symmetric per row (reading): with z the unnormalized rotated row and
+ * a = max|z| (fp32):  scale = a / fl32(7 sqrt(b)),  inv = fl32(7 / a),
+ * code = rne(z * inv) (the product exact before rounding), so the
+ * dequantized value scale * code approximates z / sqrt(b).  a == 0 gives
+ * scale 0 and codes 0.
+ * Asymmetric per group of 128 (reading): lo = min(min z, 0), hi = max(max z, 0),
+ * r = fl32(hi - lo), scale = r / fl32(15 sqrt(b)), inv = fl32(15 / r),
+ * zero = rne(-lo * inv), code = min(rne(z * inv) + zero, 15); dequantized
+ * value scale * (code - zero).  r == 0 gives scale 0, zero 0, codes 0.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef W4A4_API
+#define W4A4_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_NULL = 1,   /* a required pointer is NULL                        */
+  W4A4_ERR_SHAPE = 2,  /* a size or stride is out of range                  */
+  W4A4_ERR_ALIGN = 3,  /* a pointer or row stride is misaligned             */
+  W4A4_ERR_MODE = 4,   /* unknown mode or unsupported combination of modes  */
+  W4A4_ERR_DEVICE = 5  /* no gfx950 device, or the launch failed            */
+} w4a4_status;
+
+enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
+enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
+
+#define W4A4_ABI_VERSION 1
+
+/*
+ * rotate_quant_act - online activation step: per row of X, one fast
+ * Walsh-Hadamard transform (per 128-block or full width) fused with INT4
+ * quantization and nibble packing.
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   section "Where the rotations go" (online Hadamard per token, fused with
+ *   activation quantization); section "What it buys in 4 bits" (one scale
+ *   per token); page "SpinQuant (learned rotations + W4A4KV4)", field
+ *   "Activation scheme" (per-group asymmetric INT4).
+ *
+ *   x_f16   [M][ldx] fp16, only the first K of each row are read.
+ *   M >= 0; K >= 128, K % 128 == 0, K <= 16384; ldx >= K.
+ *   had_block  W4A4_HAD_128, or W4A4_HAD_FULL (K a power of two <= 16384;
+ *              symmetric mode only).
+ *   act_mode   W4A4_ACT_SYM_TOKEN: scales [M] fp32, zeros must be NULL.
+ *              W4A4_ACT_ASYM_G128: scales [M][K/128] fp32,
+ *              zeros [M][K/128] uint8 (must be non-NULL); had_block 128.
+ *   codes   [M][K/2] packed nibbles (written).
+ */
+W4A4_API w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
+                             int32_t had_block, int32_t act_mode,
+                             uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/*
+ * quant_weight_offline - offline weight step: rotate each output channel's
+ * row of W along K, symmetric INT4 with one scale per output channel, pack;
+ * optionally the per-128 group sums of the codes.
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   section "Where the rotations go" (weights are rotated offline, free at
+ *   run time); section "What it buys in 4 bits" (one scale per output
+ *   channel).
+ *
+ *   w_f16   [N][ldw] fp16; N >= 0 (0: no-op); K as in rotate_quant_act.
+ *   codes   [N][K/2] (written), scales [N] fp32 (written),
+ *   gsum    NULL, or [N][K/128] int32: sum of the 128 codes of each group.
+ */
+W4A4_API w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, int64_t ldw,
+                                 int32_t had_block,
+                                 uint8_t* codes, float* scales, int32_t* gsum, void* stream);
+
+/*
+ * w4a4_gemm - Y = dequant(X codes) . dequant(W codes)^T on int8 MFMA with an
+ * exact int32 accumulator (CDNA4 has no INT4 matrix instruction; the 4-bit
+ * codes are widened to int8 in registers).
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   section "A rotation changes nothing, and that is the point" (the product
+ *   of the rotated operands is X W^T); section "What it buys in 4 bits".
+ *
+ *   act_mode W4A4_ACT_SYM_TOKEN:
+ *       Y[m][n] = fl32( fl32(x_scales[m] * w_scales[n]) * acc[m][n] ),
+ *       acc = sum_k qx[m][k] * qw[n][k]; x_zeros and w_gsum are ignored.
+ *   act_mode W4A4_ACT_ASYM_G128 (x_zeros, x_scales [M][K/128]):
+ *       Y[m][n] = w_scales[n] * sum_g x_scales[m][g] * A_g[m][n],
+ *       A_g = sum_{k in group g} (qx[m][k] - x_zeros[m][g]) * qw[n][k]
+ *       (exact integer per group, summed over groups in fp32).
+ *       w_gsum is not read (the zero-point is removed from the codes before
+ *       the product) and may be NULL.
+ *   x_codes [M][K/2], w_codes [N][K/2], y [M][ldy] fp32 (written).
+ *   M >= 0, N >= 1, K >= 128, K % 128 == 0, K <= 131072, ldy >= N.
+ *   M <= 16 uses a weight-streaming kernel, larger M the tiled MFMA kernel;
+ *   both compute the same values.
+ */
+W4A4_API w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, const uint8_t* x_zeros,
+                      int32_t act_mode, const uint8_t* w_codes, const float* w_scales,
+                      const int32_t* w_gsum, int64_t M, int64_t N, int64_t K,
+                      float* y, int64_t ldy, void* stream);
+
+/*
+ * kv_rotate_quant4 - KV-cache step: every (b, h, s) head vector of D = 128
+ * fp16 values is rotated by one 128-point Hadamard and quantized to
+ * asymmetric INT4 with one (scale, zero) per vector.
+ *   Page "QuaRot (rotation-based outlier removal, W4A4KV4)", field
+ *   "Activation scheme" (the KV cache is rotated); page "SpinQuant (learned
+ *   rotations + W4A4KV4)", field "Activation scheme" (per-group asymmetric
+ *   INT4 on the KV cache, 4-bit KV).
+ *
+ *   kv_f16  element (b,h,s,d) at b*stride_b + h*stride_h + s*stride_s + d
+ *           (strides in elements, multiples of 8; d contiguous).
+ *   D == 128; B, H, S >= 0; B*H*S < 2^31.
+ *   codes  [B][H][S][64], scales [B][H][S] fp32, zeros [B][H][S] uint8 (written,
+ *          dense).
+ */
+W4A4_API w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64_t S, int64_t D,
+                             int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                             uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
+
+/* Message of the last failed call on this thread ("" after a success). */
+W4A4_API const char* w4a4_last_error(void);
+
+/* W4A4_ABI_VERSION of the loaded library. */
+W4A4_API int32_t w4a4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

@@ -1,0 +1,151 @@
+"""MI355X (gfx950) W4A4 rotate / quantize / GEMM path.
+
+Thin Python layer over the C ABI in include/w4a4.h (libw4a4.so): it checks
+tensor dtypes and devices, allocates outputs with torch, passes raw device
+pointers and the current HIP stream, and turns a non-OK status into an
+exception.  Every step of the computation runs in the library's kernels.
+
+    codes, scales, zeros = rotate_quant_act(x, had_block=128, act_mode="sym")
+    wq, ws, gsum = quant_weight_offline(w, had_block=128)
+    y = w4a4_gemm(codes, scales, zeros, wq, ws, act_mode="sym")
+    kc, ks, kz = kv_rotate_quant4(kv)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HAD_FULL,  # noqa: F401
+                   last_error)
+
+__all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
+           "abi_version", "W4A4Error"]
+
+_MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
+
+
+class W4A4Error(RuntimeError):
+    pass
+
+
+def _check(status: int, name: str) -> None:
+    if status == _lib.W4A4_OK:
+        return
+    msg = f"{name}: {_lib.STATUS_NAMES.get(status, status)}: {last_error()}"
+    if status == _lib.W4A4_ERR_DEVICE:
+        raise W4A4Error(msg)
+    raise ValueError(msg)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def abi_version() -> int:
+    return int(_lib.load().w4a4_abi_version())
+
+
+def rotate_quant_act(x: torch.Tensor, had_block: int = 128, act_mode: str = "sym"):
+    """Rotate every row of fp16 X [M, K] and quantize it to packed INT4.
+
+    Returns (codes uint8 [M, K/2], scales fp32 [M] or [M, K/128],
+    zeros uint8 [M, K/128] or None).
+    """
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    M, K = x.shape
+    mode = _MODES[act_mode]
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if mode == W4A4_ACT_SYM_TOKEN:
+        scales = torch.empty((M,), dtype=torch.float32, device=dev)
+        zeros = None
+    else:
+        scales = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        zeros = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
+    hb = W4A4_HAD_128 if had_block == 128 else (W4A4_HAD_FULL if had_block in (0, K, "full") else -1)
+    st = _lib.call("rotate_quant_act", _ptr(x), M, K, x.stride(0), hb, mode, _ptr(codes),
+                   _ptr(scales), _ptr(zeros), _stream(dev))
+    _check(st, "rotate_quant_act")
+    return codes, scales, zeros
+
+
+def quant_weight_offline(w: torch.Tensor, had_block: int = 128, with_gsum: bool = True):
+    """Rotate and quantize fp16 W [N, K] per output channel.
+
+    Returns (codes uint8 [N, K/2], scales fp32 [N], gsum int32 [N, K/128] or None).
+    """
+    _need(w, torch.float16, "w")
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D with contiguous rows")
+    N, K = w.shape
+    dev = w.device
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N,), dtype=torch.float32, device=dev)
+    gsum = torch.empty((N, K // 128), dtype=torch.int32, device=dev) if with_gsum else None
+    hb = W4A4_HAD_128 if had_block == 128 else (W4A4_HAD_FULL if had_block in (0, K, "full") else -1)
+    st = _lib.call("quant_weight_offline", _ptr(w), N, K, w.stride(0), hb, _ptr(codes),
+                   _ptr(scales), _ptr(gsum), _stream(dev))
+    _check(st, "quant_weight_offline")
+    return codes, scales, gsum
+
+
+def w4a4_gemm(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum=None, act_mode: str = "sym",
+              out: torch.Tensor | None = None):
+    """Y fp32 [M, N] from packed INT4 activations and weights (see include/w4a4.h)."""
+    _need(x_codes, torch.uint8, "x_codes")
+    _need(w_codes, torch.uint8, "w_codes")
+    _need(x_scales, torch.float32, "x_scales")
+    _need(w_scales, torch.float32, "w_scales")
+    mode = _MODES[act_mode]
+    if x_zeros is not None:
+        _need(x_zeros, torch.uint8, "x_zeros")
+    for t, n in ((x_codes, "x_codes"), (w_codes, "w_codes"), (x_scales, "x_scales"),
+                 (w_scales, "w_scales")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    M, K2 = x_codes.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K2:
+        raise ValueError("x_codes and w_codes disagree on K")
+    dev = x_codes.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(y, torch.float32, "out")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] != N or y.stride(1) != 1:
+        raise ValueError("out must be [M, N] with contiguous rows")
+    st = _lib.call("w4a4_gemm", _ptr(x_codes), _ptr(x_scales), _ptr(x_zeros), mode, _ptr(w_codes),
+                   _ptr(w_scales), _ptr(w_gsum), M, N, 2 * K2, _ptr(y), y.stride(0), _stream(dev))
+    _check(st, "w4a4_gemm")
+    return y
+
+
+def kv_rotate_quant4(kv: torch.Tensor):
+    """Rotate + asymmetric INT4 of a KV cache [B, H, S, 128] fp16 (last dim contiguous).
+
+    Returns (codes uint8 [B, H, S, 64], scales fp32 [B, H, S], zeros uint8 [B, H, S]).
+    """
+    _need(kv, torch.float16, "kv")
+    if kv.dim() != 4 or kv.stride(3) != 1:
+        raise ValueError("kv must be [B, H, S, D] with D contiguous")
+    B, H, S, D = kv.shape
+    dev = kv.device
+    codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    zeros = torch.empty((B, H, S), dtype=torch.uint8, device=dev)
+    sb, sh, ss, _ = kv.stride()
+    st = _lib.call("kv_rotate_quant4", _ptr(kv), B, H, S, D, sb, sh, ss, _ptr(codes), _ptr(scales),
+                   _ptr(zeros), _stream(dev))
+    _check(st, "kv_rotate_quant4")
+    return codes, scales, zeros

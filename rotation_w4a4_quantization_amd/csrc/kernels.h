@@ -1,0 +1,53 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+enum { kModeSym = 0, kModeAsym = 1 };
+
+// Rotate + quantize: one row of K fp16 values -> K/2 code bytes.
+struct RQParams {
+  const uint16_t* x;
+  uint8_t* codes;    // [rows][K/2]
+  float* scales;     // sym: [rows]; asym: [rows][K/128]
+  uint8_t* zeros;    // asym: [rows][K/128]
+  int32_t* gsum;     // optional: [rows][K/128]
+  int64_t rows;
+  int64_t ss;        // row stride in elements (strided mode: the s stride)
+  int64_t sh, sb;    // strided mode: h and b strides (elements)
+  uint32_t S, H;     // strided mode: row r -> (b, h, s) = (r/(H S), (r/S)%H, r%S)
+  int32_t K;
+  int32_t nb;        // K / 128 (set by the launcher)
+  int32_t seg;       // threads per row slot (set by the launcher)
+  int32_t rows_per_wg;
+  float cdiv;        // fl32(7 sqrt(b)) (sym) or fl32(15 sqrt(b)) (asym)
+};
+
+struct RQGeometry {
+  int seg, rows_per_wg, threads;
+  int64_t grid;
+};
+
+RQGeometry rq_geometry(int64_t rows, int K);
+hipError_t launch_rotate_quant(RQParams p, int mode, bool full, bool gsum, bool strided,
+                               hipStream_t st);
+
+// W4A4 GEMM: y[M][ldy] = dequant(xq) . dequant(wq)^T.
+struct GemmParams {
+  const uint8_t* xq;    // [M][K/2]
+  const float* xs;      // sym: [M]; asym: [M][K/128]
+  const uint8_t* xz;    // asym: [M][K/128]
+  const uint8_t* wq;    // [N][K/2]
+  const float* ws;      // [N]
+  float* y;
+  int64_t M, N, ldy;
+  int32_t K;
+};
+
+hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st);
+hipError_t gemm_prepare_device();   // once per device, before the first GEMM launch
+
+}  // namespace w4a4

@@ -1,0 +1,337 @@
+// Fused fast Walsh-Hadamard transform + INT4 quantization + nibble packing.
+//
+// One kernel serves the online activation step, the offline weight step and
+// the KV-cache step:
+//   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+//   section "Where the rotations go": a rotation that cannot be folded into
+//   the weights costs one fast Hadamard transform per token, so it is fused
+//   with the quantization of the activations; section "What it buys in 4
+//   bits": one INT4 scale per token (per output channel for weights).
+//   Page "SpinQuant (learned rotations + W4A4KV4)", field "Activation
+//   scheme": per-group asymmetric INT4 for activations and the KV cache.
+//
+// Data layout in registers.  A 128-element Hadamard block of a row is held by
+// a quad of 4 lanes; lane q of the quad loads the four 16-byte chunks
+// q, q+4, q+8, q+12 of the block, so element k = 32r + 8q + e (r, e: register
+// coordinates) sits in register 8r + e of lane q.  The transform is the
+// tensor product of 2x2 butterflies over the 7 index bits, and butterflies on
+// different bits commute, so the 5 bits held in registers (e: bits 0-2,
+// r: bits 5-6) are done in registers and the 2 lane bits (q: bits 3-4) with
+// DPP quad permutes.  A full-width transform (block = K) continues over the
+// block index through LDS.  The row's absmax (symmetric) or each block's
+// min/max (asymmetric) is reduced across lanes, then every value is turned
+// into a code with one fma against a magic constant (round to nearest even
+// of the exact product z * inv) and 8 codes are packed per dword.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a4 {
+
+namespace {
+
+template <int LOG_N>
+__device__ __forceinline__ void fwht_regs(float* v) {
+  // In-register butterflies over bits 0..LOG_N-1 of the array index.
+#pragma unroll
+  for (int b = 1; b < (1 << LOG_N); b <<= 1) {
+#pragma unroll
+    for (int i = 0; i < (1 << LOG_N); ++i) {
+      if (!(i & b)) {
+        const float a = v[i], c = v[i | b];
+        v[i] = a + c;
+        v[i | b] = a - c;
+      }
+    }
+  }
+}
+
+// Remaining butterflies of a full-width transform: FWHT over the block index
+// (nb = 2^LOG_NB blocks of 128) of one row held in LDS as [nb][128] floats.
+// T = 4 nb threads of the row slot take part; every pass reads, transforms
+// and writes back 32 values per thread.
+template <int LOG_NB>
+__device__ __forceinline__ void fwht_block_axis(float* buf, int lt) {
+  constexpr int NB = 1 << LOG_NB;
+  constexpr int T = 4 * NB;
+  constexpr int LA = LOG_NB < 5 ? LOG_NB : 5;         // pass A: block bits 0..LA-1
+  constexpr int NA = 1 << LA;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32 / NA; ++j) {
+    const int it = lt + T * j;
+    const int c = it & 127, grp = it >> 7;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) v[j * NA + t] = buf[(grp * NA + t) * 128 + c];
+  }
+#pragma unroll
+  for (int j = 0; j < 32 / NA; ++j) fwht_regs<LA>(v + j * NA);
+#pragma unroll
+  for (int j = 0; j < 32 / NA; ++j) {
+    const int it = lt + T * j;
+    const int c = it & 127, grp = it >> 7;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) buf[(grp * NA + t) * 128 + c] = v[j * NA + t];
+  }
+  if constexpr (LOG_NB > 5) {
+    constexpr int LB = LOG_NB - 5;                    // pass B: block bits 5..LOG_NB-1
+    constexpr int NBB = 1 << LB;
+    constexpr int ITEMS = 4096 / T;                   // (128 columns x 32 low block indices) / T
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int it = lt + T * j;
+      const int c = it & 127, lo = it >> 7;
+#pragma unroll
+      for (int t = 0; t < NBB; ++t) v[j * NBB + t] = buf[(lo + 32 * t) * 128 + c];
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) fwht_regs<LB>(v + j * NBB);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int it = lt + T * j;
+      const int c = it & 127, lo = it >> 7;
+#pragma unroll
+      for (int t = 0; t < NBB; ++t) buf[(lo + 32 * t) * 128 + c] = v[j * NBB + t];
+    }
+  }
+}
+
+// Pack 8 codes whose value sits in the low 4 bits of each word (bits 4..7
+// zero, higher bits ignored) into one dword, element 0 in bits 3:0.
+__device__ __forceinline__ uint32_t pack8(const uint32_t* b) {
+  const uint32_t p01 = (b[1] << 4) | b[0];
+  const uint32_t p23 = (b[3] << 4) | b[2];
+  const uint32_t p45 = (b[5] << 4) | b[4];
+  const uint32_t p67 = (b[7] << 4) | b[6];
+  const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);   // [p01.b0, p23.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p67, p45, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                   // [lo.b0, lo.b1, hi.b0, hi.b1]
+}
+
+}  // namespace
+
+template <int MODE, int LOG_NB_FULL, bool GSUM, bool STRIDED>
+__global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
+  extern __shared__ float lds[];
+  const int tid = threadIdx.x;
+  const int slot = tid / p.seg;
+  const int lt = tid - slot * p.seg;
+  const int64_t row = (int64_t)blockIdx.x * p.rows_per_wg + slot;
+  const int blk = lt >> 2;
+  const int q = lt & 3;
+  const bool valid = (row < p.rows) && (blk < p.nb);
+
+  int64_t roff;
+  if constexpr (STRIDED) {
+    const uint32_t r = (uint32_t)row;
+    const uint32_t s = r % p.S, t = r / p.S;
+    const uint32_t h = t % p.H, b = t / p.H;
+    roff = (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)s * p.ss;
+  } else {
+    roff = row * p.ss;
+  }
+
+  // ---- load 32 fp16 values: chunks q, q+4, q+8, q+12 of block `blk`
+  float v[32];
+  {
+    const uint16_t* src = p.x + roff + blk * 128 + q * 8;
+    uint4 w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      w[r] = valid ? *reinterpret_cast<const uint4*>(src + 32 * r) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t d[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * r + 2 * j] = h2f(d[j] & 0xFFFFu);
+        v[8 * r + 2 * j + 1] = h2f(d[j] >> 16);
+      }
+    }
+  }
+
+  // ---- 128-point FWHT: 5 register bits, then the 2 quad-lane bits by DPP
+  fwht_regs<5>(v);
+  {
+    const float s0 = (q & 1) ? -1.0f : 1.0f;   // high half of the pair keeps partner - self
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = fmaf(v[i], s0, dpp_f<0xB1>(v[i]));
+    const float s1 = (q & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = fmaf(v[i], s1, dpp_f<0x4E>(v[i]));
+  }
+
+  // ---- full width: butterflies over the block index through LDS
+  if constexpr (LOG_NB_FULL > 0) {
+    float* buf = lds + (size_t)slot * p.K;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4* dst = reinterpret_cast<float4*>(buf + blk * 128 + 32 * r + 8 * q);
+      dst[0] = make_float4(v[8 * r + 0], v[8 * r + 1], v[8 * r + 2], v[8 * r + 3]);
+      dst[1] = make_float4(v[8 * r + 4], v[8 * r + 5], v[8 * r + 6], v[8 * r + 7]);
+    }
+    __syncthreads();
+    fwht_block_axis<LOG_NB_FULL>(buf, lt);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4* s4 = reinterpret_cast<const float4*>(buf + blk * 128 + 32 * r + 8 * q);
+      const float4 a = s4[0], b = s4[1];
+      v[8 * r + 0] = a.x; v[8 * r + 1] = a.y; v[8 * r + 2] = a.z; v[8 * r + 3] = a.w;
+      v[8 * r + 4] = b.x; v[8 * r + 5] = b.y; v[8 * r + 6] = b.z; v[8 * r + 7] = b.w;
+    }
+    __syncthreads();   // the row buffer is reused for the reduction below
+  }
+
+  const int64_t crow = row * (int64_t)(p.K / 2);
+  uint32_t words[4];
+
+  if constexpr (MODE == kModeSym) {
+    // ---- per-row absmax
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = quad_max(am);
+    if (p.seg <= kWave) {
+      for (int m = 4; m < p.seg; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+    } else {
+      for (int m = 4; m < kWave; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+      float* red = lds;
+      const int nw = p.seg / kWave;
+      if ((lt & (kWave - 1)) == 0) red[slot * 16 + (lt / kWave)] = am;
+      __syncthreads();
+      am = 0.0f;
+      for (int w = 0; w < nw; ++w) am = fmaxf(am, red[slot * 16 + w]);
+    }
+    const float inv = am > 0.0f ? div_rn(7.0f, am) : 0.0f;
+    // codes: fma gives 2^23*1.5 + 8 + rne(z*inv); the low nibble is the code
+    // in offset-8 binary, turned into two's complement by the final xor.
+    int gs = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        b[e] = fbits(fmaf(v[8 * r + e], inv, kRneMagic + 8.0f));
+        if constexpr (GSUM) gs += (int)(b[e] - (kRneMagicBits + 8u));
+      }
+      words[r] = pack8(b) ^ 0x88888888u;
+    }
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r + 4 * q) = words[r];
+      if (lt == 0) p.scales[row] = am > 0.0f ? div_rn(am, p.cdiv) : 0.0f;
+    }
+    if constexpr (GSUM) {
+      gs = quad_sum(gs);
+      if (valid && q == 0) p.gsum[row * p.nb + blk] = gs;
+    }
+  } else {
+    // ---- asymmetric, one group per 128-block
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
+    }
+    lo = quad_min(lo);
+    hi = quad_max(hi);
+    const float rg = hi - lo;
+    const float inv = rg > 0.0f ? div_rn(15.0f, rg) : 0.0f;
+    int zp = (int)(fbits(fmaf(-lo, inv, kRneMagic)) - kRneMagicBits);
+    zp = zp < 0 ? 0 : (zp > 15 ? 15 : zp);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t u = fbits(fmaf(v[8 * r + e], inv, kRneMagic)) + (uint32_t)zp;
+        b[e] = u < kRneMagicBits + 15u ? u : kRneMagicBits + 15u;
+      }
+      words[r] = pack8(b);
+    }
+    if (valid) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r + 4 * q) = words[r];
+      if (q == 0) {
+        p.scales[row * p.nb + blk] = rg > 0.0f ? div_rn(rg, p.cdiv) : 0.0f;
+        p.zeros[row * p.nb + blk] = (uint8_t)zp;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+namespace {
+
+template <int MODE, int LOGF, bool GSUM, bool STRIDED>
+hipError_t launch_t(const RQParams& p, int threads, size_t lds, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED>), dim3((uint32_t)grid),
+                     dim3(threads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <bool GSUM>
+hipError_t launch_full(const RQParams& p, int logf, int threads, size_t lds, int64_t grid,
+                       hipStream_t st) {
+  switch (logf) {
+    case 1: return launch_t<kModeSym, 1, GSUM, false>(p, threads, lds, grid, st);
+    case 2: return launch_t<kModeSym, 2, GSUM, false>(p, threads, lds, grid, st);
+    case 3: return launch_t<kModeSym, 3, GSUM, false>(p, threads, lds, grid, st);
+    case 4: return launch_t<kModeSym, 4, GSUM, false>(p, threads, lds, grid, st);
+    case 5: return launch_t<kModeSym, 5, GSUM, false>(p, threads, lds, grid, st);
+    case 6: return launch_t<kModeSym, 6, GSUM, false>(p, threads, lds, grid, st);
+    case 7: return launch_t<kModeSym, 7, GSUM, false>(p, threads, lds, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+RQGeometry rq_geometry(int64_t rows, int K) {
+  RQGeometry g{};
+  const int nb = K / 128;
+  const int T = 4 * nb;
+  if (T <= kWave) {
+    int seg = 4;
+    while (seg < T) seg <<= 1;
+    g.seg = seg;
+    g.rows_per_wg = 256 / seg;
+  } else {
+    g.seg = (T + kWave - 1) / kWave * kWave;
+    g.rows_per_wg = g.seg >= 256 ? 1 : 256 / g.seg;
+  }
+  g.threads = g.seg * g.rows_per_wg;
+  g.grid = (rows + g.rows_per_wg - 1) / g.rows_per_wg;
+  return g;
+}
+
+hipError_t launch_rotate_quant(RQParams p, int mode, bool full, bool gsum, bool strided,
+                               hipStream_t st) {
+  const RQGeometry g = rq_geometry(p.rows, p.K);
+  p.seg = g.seg;
+  p.rows_per_wg = g.rows_per_wg;
+  p.nb = p.K / 128;
+  int logf = 0;
+  if (full && p.nb > 1) {
+    while ((1 << logf) < p.nb) ++logf;
+  }
+  size_t lds = 0;
+  if (logf > 0) lds = (size_t)g.rows_per_wg * p.K * sizeof(float);
+  else if (mode == kModeSym && g.seg > kWave) lds = (size_t)g.rows_per_wg * 16 * sizeof(float);
+  if (g.grid == 0) return hipSuccess;
+  if (mode == kModeSym) {
+    if (strided) return hipErrorInvalidValue;
+    if (logf > 0) return gsum ? launch_full<true>(p, logf, g.threads, lds, g.grid, st)
+                              : launch_full<false>(p, logf, g.threads, lds, g.grid, st);
+    return gsum ? launch_t<kModeSym, 0, true, false>(p, g.threads, lds, g.grid, st)
+                : launch_t<kModeSym, 0, false, false>(p, g.threads, lds, g.grid, st);
+  }
+  if (gsum || logf > 0) return hipErrorInvalidValue;
+  return strided ? launch_t<kModeAsym, 0, false, true>(p, g.threads, lds, g.grid, st)
+                 : launch_t<kModeAsym, 0, false, false>(p, g.threads, lds, g.grid, st);
+}
+
+}  // namespace w4a4

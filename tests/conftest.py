@@ -10,3 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name every GPU case on stderr before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

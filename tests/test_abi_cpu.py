@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rotation_w4a4_quantization_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"W4A4_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
+              "w4a4_last_error", "w4a4_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert lib.w4a4_abi_version() == 1
+    src = open(HEADER).read()
+    assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
+
+
+def test_no_internal_symbols_exported():
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read().split("\n")
+    names = {ln.split()[-1] for ln in out if ln.strip() and ln.split()[1] in ("T", "W")}
+    names = {n for n in names if not n.startswith("_")}
+    assert names == set(_declared())
+
+
+class _Buf:
+    """16-byte aligned host scratch used only as a non-NULL pointer value
+    (validation fails before anything is read)."""
+
+    def __init__(self, n=1 << 16):
+        self.raw = ctypes.create_string_buffer(n + 32)
+        self.a = (ctypes.addressof(self.raw) + 15) // 16 * 16
+
+
+B = _Buf()
+A = B.a
+NUL = None
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, 4, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, 0, NUL, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, 0, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 100, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # K % 128
+    ((A, 4, 0, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 32768, 32768, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # K > 16384
+    ((A, -1, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 256, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # ldx < K
+    ((A, 4, 384, 384, 0, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),         # full needs 2^p
+    ((A, 4, 128, 132, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),       # ldx % 8
+    ((A + 2, 4, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 4, 128, 128, 64, 0, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),         # had_block
+    ((A, 4, 128, 128, 128, 2, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # act_mode
+    ((A, 4, 128, 128, 128, 0, A, A, A, NUL), _lib.W4A4_ERR_MODE),          # zeros in sym
+    ((A, 4, 128, 128, 128, 1, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # no zeros in asym
+    ((A, 4, 256, 256, 0, 1, A, A, A, NUL), _lib.W4A4_ERR_MODE),            # asym + full
+    ((A, 0, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_OK),              # M == 0: no-op
+    ((NUL, 0, 128, 128, 128, 0, NUL, NUL, NUL, NUL), _lib.W4A4_OK),        # M == 0, NULL buffers
+    ((NUL, 0, 100, 128, 128, 0, NUL, NUL, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # sizes still checked
+])
+def test_rotate_quant_act_validation(args, status):
+    assert _lib.call("rotate_quant_act", *args) == status
+    assert (_lib.last_error() == "") == (status == _lib.W4A4_OK)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, 4, 128, 128, 128, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 200, 200, 128, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 128, 128, 7, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),
+    ((A, 4, 128, 128, 128, A, A, A + 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 0, 128, 128, 128, A, A, A, NUL), _lib.W4A4_OK),
+])
+def test_quant_weight_offline_validation(args, status):
+    assert _lib.call("quant_weight_offline", *args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, A, NUL, 0, A, A, NUL, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, NUL, 0, A, A, NUL, 4, 4, 128, NUL, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, NUL, 1, A, A, NUL, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_MODE),   # asym without zeros
+    ((A, A, NUL, 3, A, A, NUL, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_MODE),
+    ((A, A, NUL, 0, A, A, NUL, 4, 0, 128, A, 4, NUL), _lib.W4A4_ERR_SHAPE),  # N == 0
+    ((A, A, NUL, 0, A, A, NUL, 4, 4, 96, A, 4, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A, NUL, 0, A, A, NUL, 4, 4, 128, A, 3, NUL), _lib.W4A4_ERR_SHAPE),  # ldy < N
+    ((A, A, NUL, 0, A, A, NUL, 4, 4, 262144, A, 4, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A, NUL, 0, A + 8, A, NUL, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, A, NUL, 0, A, A, NUL, 0, 4, 128, A, 4, NUL), _lib.W4A4_OK),        # M == 0: no-op
+    ((NUL, NUL, NUL, 0, NUL, NUL, NUL, 0, 4, 128, NUL, 4, NUL), _lib.W4A4_OK),
+])
+def test_gemm_validation(args, status):
+    assert _lib.call("w4a4_gemm", *args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, 1, 1, 1, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 1, 1, 1, 128, 128, 128, 128, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 1, 1, 1, 64, 64, 64, 64, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),      # D != 128
+    ((A, -1, 1, 1, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 1, 1, 1, 128, 128, 128, 124, A, A, A, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 1 << 16, 1 << 10, 1 << 6, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 0, 4, 4, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_OK),
+])
+def test_kv_validation(args, status):
+    assert _lib.call("kv_rotate_quant4", *args) == status
+
+
+def test_no_device_is_a_device_error():
+    """Valid arguments on a machine without a gfx950 GPU: W4A4_ERR_DEVICE, nothing launched."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _lib.call("rotate_quant_act", A, 4, 128, 128, 128, 0, A, A, NUL, NUL)
+    assert st == _lib.W4A4_ERR_DEVICE
+    assert "device" in _lib.last_error()
