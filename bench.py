@@ -82,6 +82,120 @@ def cpu_baseline(reps: int = 3) -> dict:
                       f"{dt:.3f} s per step, numpy float64 + BLAS"}
 
 
+def _time_kernel(torch, fn, flush, n=30, warm_n=50):
+    """Median / p10 / p90 of one launch after flushing the caches (cold), and
+    the mean of back-to-back launches (warm)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    cold = []
+    for _ in range(n):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold.sort()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(warm_n):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return dict(cold_ms_median=cold[len(cold) // 2], cold_ms_p10=cold[len(cold) // 10],
+                cold_ms_p90=cold[(9 * len(cold)) // 10], warm_ms=a.elapsed_time(b) / warm_n)
+
+
+def run_suite(torch, R, WL):
+    """One JSON line per (entry point, configuration): cold (caches flushed by
+    writing 512 MiB) and warm timings, with the roofline each kernel answers to."""
+    dev = torch.device("cuda:0")
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        scratch.fill_(1)
+
+    def emit(kernel, config, t, nbytes=None, ops=None):
+        rec = dict(kernel=kernel, config=config, **{k: round(v, 5) for k, v in t.items()})
+        if nbytes is not None:
+            gbs = nbytes / (t["cold_ms_median"] * 1e-3) / 1e9
+            rec.update(bytes=nbytes, bound="hbm", cold_GBps=round(gbs, 1),
+                       cold_frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                       warm_GBps=round(nbytes / (t["warm_ms"] * 1e-3) / 1e9, 1))
+        if ops is not None:
+            tops = ops / (t["cold_ms_median"] * 1e-3) / 1e12
+            rec.update(ops=ops, bound="mfma", cold_TOPS=round(tops, 1),
+                       cold_frac_int8=round(tops / INT8_PEAK_TOPS, 4),
+                       warm_TOPS=round(ops / (t["warm_ms"] * 1e-3) / 1e12, 1))
+        print(json.dumps(rec), flush=True)
+
+    def T(a):
+        return torch.from_numpy(a).to(dev)
+
+    def act_bytes(M, K, asym=False):
+        return 2 * M * K + M * K // 2 + (5 * M * (K // 128) if asym else 4 * M)
+
+    # q_proj family M x 4096 x 4096 (both Hadamard widths), decode rows, down_proj, gate/up
+    wq = T(WL.qproj_weight())
+    for block in (128, "full"):
+        tag = "128" if block == 128 else "full"
+        wc, ws, wg = R.quant_weight_offline(wq, block)
+        emit("quant_weight_offline", f"qproj W 4096x4096 had{tag}",
+             _time_kernel(torch, lambda: R.quant_weight_offline(wq, block), flush),
+             nbytes=2 * 4096 * 4096 + 4096 * 2048 + 4 * 4096 + 4 * 4096 * 32)
+        for M in (1, 4, 16, 256, 2048, 8192, 32768):
+            x = T(WL.qproj(M=min(M, 2048), with_w=False)["X"])
+            if M > 2048:
+                x = x.repeat(M // 2048, 1)
+            xc, xs, _ = R.rotate_quant_act(x, block)
+            emit("rotate_quant_act", f"qproj X {M}x4096 had{tag}",
+                 _time_kernel(torch, lambda: R.rotate_quant_act(x, block), flush), nbytes=act_bytes(M, 4096))
+            y = torch.empty((M, 4096), dtype=torch.float32, device=dev)
+            emit("w4a4_gemm", f"{M}x4096x4096 had{tag}",
+                 _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y), flush),
+                 nbytes=(M * 2048 + 4 * M + 4096 * 2048 + 4 * 4096 + 4 * M * 4096) if M <= 16 else None,
+                 ops=2 * M * 4096 * 4096)
+    del wq
+    d = WL.downproj()
+    x, w = T(d["X"]), T(d["W"])
+    del d
+    xc, xs, _ = R.rotate_quant_act(x, 128)
+    wc, ws, _ = R.quant_weight_offline(w, 128)
+    emit("rotate_quant_act", "downproj X 4096x14336 had128",
+         _time_kernel(torch, lambda: R.rotate_quant_act(x, 128), flush), nbytes=act_bytes(4096, 14336))
+    emit("quant_weight_offline", "downproj W 4096x14336 had128",
+         _time_kernel(torch, lambda: R.quant_weight_offline(w, 128), flush),
+         nbytes=2 * 4096 * 14336 + 4096 * 7168 + 4 * 4096 + 4 * 4096 * 112)
+    y = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+    emit("w4a4_gemm", "downproj 4096x4096x14336",
+         _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y), flush),
+         ops=2 * 4096 * 4096 * 14336)
+    del x, w, xc, wc, y
+    d = WL.gateup()
+    x, w = T(d["X"]), T(d["W"])
+    del d
+    xc, xs, xz = R.rotate_quant_act(x, 128, "asym")
+    wc, ws, _ = R.quant_weight_offline(w, 128)
+    emit("rotate_quant_act", "gateup X 8192x8192 asym g128",
+         _time_kernel(torch, lambda: R.rotate_quant_act(x, 128, "asym"), flush),
+         nbytes=act_bytes(8192, 8192, asym=True))
+    emit("quant_weight_offline", "gateup W 28672x8192 had128",
+         _time_kernel(torch, lambda: R.quant_weight_offline(w, 128), flush, n=10),
+         nbytes=2 * 28672 * 8192 + 28672 * 4096 + 4 * 28672 + 4 * 28672 * 64)
+    y = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
+    emit("w4a4_gemm", "gateup asym 8192x28672x8192",
+         _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, xz, wc, ws, act_mode="asym", out=y), flush, n=10,
+                      warm_n=10),
+         ops=2 * 8192 * 28672 * 8192)
+    del x, w, xc, wc, y
+    kv = T(WL.kv()["KV"])
+    emit("kv_rotate_quant4", "kv 8x32x4096x128",
+         _time_kernel(torch, lambda: R.kv_rotate_quant4(kv), flush),
+         nbytes=2 * kv.numel() + kv.numel() // 2 + 5 * (kv.numel() // 128))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,8 +222,7 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     if args.suite:
-        from bench_suite import run_suite   # noqa: E402  (kept beside bench.py)
-        run_suite()
+        run_suite(torch, R, WL)
         return 0
 
     dev = torch.device("cuda:0")
