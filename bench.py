@@ -110,12 +110,13 @@ def _time_kernel(torch, fn, flush, n=30, warm_n=50):
 
 def run_suite(torch, R, WL):
     """One JSON line per (entry point, configuration): cold (caches flushed by
-    writing 512 MiB) and warm timings, with the roofline each kernel answers to."""
+    reading 512 MiB, which leaves no dirty lines to write back during the
+    timed launch) and warm timings, with the roofline each kernel answers to."""
     dev = torch.device("cuda:0")
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
     def flush():
-        scratch.fill_(1)
+        scratch.amax()
 
     def emit(kernel, config, t, nbytes=None, ops=None):
         rec = dict(kernel=kernel, config=config, **{k: round(v, 5) for k, v in t.items()})
@@ -196,6 +197,52 @@ def run_suite(torch, R, WL):
          nbytes=2 * kv.numel() + kv.numel() // 2 + 5 * (kv.numel() // 128))
 
 
+def run_only(torch, R, WL, which, steps, had):
+    """Launch one entry point `steps` times on its workload (q_proj unless named)."""
+    dev = torch.device("cuda:0")
+    block = 128 if had == "128" else "full"
+
+    def T(a):
+        return torch.from_numpy(a).to(dev)
+
+    if which == "copy":
+        # plain device copy of 256 MiB: the reference kernel for the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)                                           # noqa: E731
+    elif which in ("gemm", "act", "weight", "decode"):
+        d = WL.qproj() if which != "decode" else WL.decode(16)
+        x, w = T(d["X"]), T(d["W"])
+        wc, ws, _ = R.quant_weight_offline(w, block)
+        xc, xs, _ = R.rotate_quant_act(x, block)
+        y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.float32, device=dev)
+        fn = {"gemm": lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y),
+              "decode": lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y),
+              "act": lambda: R.rotate_quant_act(x, block),
+              "weight": lambda: R.quant_weight_offline(w, block)}[which]
+    elif which == "downproj":
+        d = WL.downproj()
+        x, w = T(d["X"]), T(d["W"])
+        wc, ws, _ = R.quant_weight_offline(w, 128)
+        xc, xs, _ = R.rotate_quant_act(x, 128)
+        y = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+        fn = lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y)                  # noqa: E731
+    elif which == "gateup":
+        d = WL.gateup()
+        x, w = T(d["X"]), T(d["W"])
+        wc, ws, _ = R.quant_weight_offline(w, 128)
+        xc, xs, xz = R.rotate_quant_act(x, 128, "asym")
+        y = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
+        fn = lambda: R.w4a4_gemm(xc, xs, xz, wc, ws, act_mode="asym", out=y)   # noqa: E731
+    else:
+        kv = T(WL.kv()["KV"])
+        fn = lambda: R.kv_rotate_quant4(kv)                                    # noqa: E731
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"ran {which} x{steps}", flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +251,8 @@ def main() -> int:
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
+    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "decode", "gateup", "downproj", "copy"],
+                    help="launch one kernel --steps times back to back (for rocprofv3 runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -223,6 +272,9 @@ def main() -> int:
         return 1
     if args.suite:
         run_suite(torch, R, WL)
+        return 0
+    if args.only:
+        run_only(torch, R, WL, args.only, args.steps, args.had)
         return 0
 
     dev = torch.device("cuda:0")

@@ -79,6 +79,7 @@ w4a4_status check_rows_k(int64_t rows, int64_t K, int64_t ld, const char* rn, co
   if (K < 128 || K % 128 != 0 || K > 16384)
     return fail(W4A4_ERR_SHAPE, "K=%lld must be a multiple of 128 in [128, 16384]", (long long)K);
   if (ld < K) return fail(W4A4_ERR_SHAPE, "%s=%lld must be >= K=%lld", ldn, (long long)ld, (long long)K);
+  if (ld >= (int64_t(1) << 24)) return fail(W4A4_ERR_SHAPE, "%s=%lld must be < 2^24 elements", ldn, (long long)ld);
   if (ld % 8 != 0) return fail(W4A4_ERR_ALIGN, "%s=%lld must be a multiple of 8 elements", ldn, (long long)ld);
   return W4A4_OK;
 }

@@ -26,11 +26,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;   // BK in 4-bit elements
-constexpr int LROW = 144;                      // LDS bytes per int8 row: 128 + 16 pad
-constexpr int TILE = 128 * LROW;               // one operand tile in LDS
-constexpr int kStageBytes = 2 * TILE;          // A + B
-constexpr int kGemmLds = 2 * kStageBytes + 2 * 128 * 4;   // 2 stages + asym row scales
+constexpr int BN = 128, BK = 128;   // BK in 4-bit elements
+constexpr int LROW = 128;                      // LDS bytes per int8 row (one K step)
+
+// LDS layout of an int8 operand row: its eight 16-byte chunks are stored at
+// chunk position c ^ s(row), s(row) = (row & 7) ^ ((row >> 3) & 1).  The
+// MFMA fragment reads (16 consecutive rows, one chunk per lane) then hit
+// distinct bank groups both within every 8 lanes and within every 16 lanes;
+// measured on gfx950 this pattern reads at ~165 B/clk/CU against ~110 for
+// 16-byte padding or a (row >> 1) swizzle.
+__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_chunk(int row, int c) { return row * LROW + ((c ^ lds_swz(row)) << 4); }
 
 __device__ __forceinline__ void widen_signed(uint32_t p, uint32_t& even16, uint32_t& odd16) {
   even16 = (p << 4) & 0xF0F0F0F0u;
@@ -47,17 +53,55 @@ __device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) 
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// 4x4 transpose inside a quad of lanes: on entry lane k of the quad holds
+// column k of a 4x4 block in y[0..3] (y[v] = row v); on exit it holds row k
+// (y[c] = column c).  Two butterflies swap a lane-index bit with a
+// register-index bit (DPP quad permutes).
+__device__ __forceinline__ void quad_transpose4(float* y, int k) {
+  {
+    const bool hi = k & 1;
+#pragma unroll
+    for (int m = 0; m < 4; m += 2) {
+      const float send = hi ? y[m] : y[m + 1];
+      const float recv = dpp_f<0xB1>(send);
+      y[m] = hi ? recv : y[m];
+      y[m + 1] = hi ? y[m + 1] : recv;
+    }
+  }
+  {
+    const bool hi = k & 2;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float send = hi ? y[m] : y[m + 2];
+      const float recv = dpp_f<0x4E>(send);
+      y[m] = hi ? recv : y[m];
+      y[m + 2] = hi ? y[m + 2] : recv;
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- tiled kernel
-// 128x128 output tile per workgroup, 4 waves of 64x64 (4x4 MFMA blocks of
-// 16x16).  Each 128-wide K step: every thread loads 4 x 16 packed bytes,
-// widens them once to int8 and writes them to the next LDS stage while the
-// waves run 32 MFMAs each on the current stage.
-template <bool ASYM>
-__global__ void __launch_bounds__(256) gemm_tile_kernel(GemmParams p) {
+// BM x 128 output tile per workgroup (BM = 128 or 256), BM/64 x 2 waves of
+// 64x64 each (4 x 4 MFMA blocks of 16x16).  K advances 128 (one asymmetric
+// group) per step.  Pipeline: while step t's MFMAs run out of one LDS stage,
+// the raw buffer loads of step t+2 are in flight into one register set and
+// step t+1's packed bytes (loaded a step earlier) are widened to int8 and
+// written to the other stage; one barrier per step.  Buffer loads past the
+// end of A or B return zero, so ragged M, N and the prefetch past the last
+// step need no branches in the main loop.
+template <int BM, bool ASYM>
+__global__ void __launch_bounds__(BM * 2)
+__attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2, ASYM ? 1 : 2))) gemm_tile_kernel(GemmParams p) {
+  constexpr int NT = BM * 2;                  // threads: BM/64 x 2 waves
+  constexpr int ROWS = BM + BN;               // operand rows per K step
+  constexpr int NCH = ROWS * 4 / NT;          // 16-byte chunks per thread per K step
+  constexpr int NCA = BM * 4 / NT;            // ... of which from A (the rest from B)
+  constexpr int ATILE = BM * LROW;
+  constexpr int STAGE = ROWS * LROW;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* sxs = reinterpret_cast<float*>(smem + 2 * kStageBytes);   // [2][128] asym row scales
+  float* sxs = reinterpret_cast<float*>(smem + 2 * STAGE);   // asym: [2][BM] row scales / 16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,61 +114,61 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(GemmParams p) {
   const int64_t ldc = p.K / 2;   // packed bytes per row
   const int G = nkt;
 
-  // loader coordinates: 4 chunks of 16 packed bytes per thread
-  const int lrow = tid >> 2, lc = tid & 3;
-  const uint8_t* gptr[4];
-  bool gval[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = lrow + 64 * (j & 1);
-    if (j < 2) {
-      gval[j] = m0 + row < p.M;
-      gptr[j] = p.xq + (gval[j] ? (m0 + row) : 0) * ldc + 16 * lc;
-    } else {
-      gval[j] = n0 + row < p.N;
-      gptr[j] = p.wq + (gval[j] ? (n0 + row) : 0) * ldc + 16 * lc;
-    }
-  }
+  // buffer resources covering rows m0.. of A and n0.. of B (reads past the end give 0)
+  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
 
-  uint4 g[4];
-  uint32_t zx4[2] = {0u, 0u};
-  float sxn = 0.0f;
-  auto gload = [&](int kt) {
+  uint4 g0[NCH], g1[NCH];
+  uint32_t z0[NCH], z1[NCH];
+  float sx0 = 0.0f, sx1 = 0.0f;
+  auto gload = [&](uint4* g, uint32_t* z, float& sxn, int kt) {
+    const int kc = kt < nkt ? kt : nkt - 1;       // clamped index for the side arrays
+    // chunk j < NCA comes from A, the others from B (ci = tid + NT j runs over
+    // the BM A rows first, then the 128 B rows)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      g[j] = gval[j] ? *reinterpret_cast<const uint4*>(gptr[j] + kt * 64) : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (ASYM) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t row = m0 + lrow + 64 * j;
-        zx4[j] = gval[j] ? (uint32_t)p.xz[row * G + kt] * 0x01010101u : 0u;
+    for (int j = 0; j < NCH; ++j) {
+      const int ci = tid + NT * j;
+      const int row = ci >> 2, c = ci & 3;
+      if (j < NCA) {
+        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            ra, row * (int)ldc + 16 * c + kt * 64, 0, 0));
+        if constexpr (ASYM) {
+          const int64_t grow = m0 + row;
+          z[j] = grow < p.M ? (uint32_t)p.xz[grow * G + kc] * 0x01010101u : 0u;
+        }
+      } else {
+        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (row - BM) * (int)ldc + 16 * c + kt * 64, 0, 0));
       }
-      if (tid < 128) sxn = (m0 + tid < p.M) ? p.xs[(m0 + tid) * G + kt] * 0.0625f : 0.0f;
     }
+    if constexpr (ASYM) sxn = (tid < BM && m0 + tid < p.M) ? p.xs[(m0 + tid) * G + kc] * 0.0625f : 0.0f;
   };
-  auto lstore = [&](int stage) {
-    uint8_t* base = smem + stage * kStageBytes;
+  auto lstore = [&](const uint4* g, const uint32_t* z, float sxn, int stage) {
+    uint8_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = lrow + 64 * (j & 1);
-      uint8_t* dst = base + (j >> 1) * TILE + row * LROW + 32 * lc;
+    for (int j = 0; j < NCH; ++j) {
+      const int ci = tid + NT * j;
       const uint32_t w[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
       uint32_t o[8];
-      if (ASYM && j < 2) {
+      if (ASYM && j < NCA) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          o[2 * d] = levels(w[d] & 0x0F0F0F0Fu, zx4[j]);
-          o[2 * d + 1] = levels((w[d] >> 4) & 0x0F0F0F0Fu, zx4[j]);
+          o[2 * d] = levels(w[d] & 0x0F0F0F0Fu, z[j]);
+          o[2 * d + 1] = levels((w[d] >> 4) & 0x0F0F0F0Fu, z[j]);
         }
       } else {
 #pragma unroll
         for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
       }
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      const int row = ci >> 2, c = 2 * (ci & 3);
+      *reinterpret_cast<uint4*>(base + lds_chunk(row, c)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(base + lds_chunk(row, c + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
     }
     if constexpr (ASYM) {
-      if (tid < 128) sxs[stage * 128 + tid] = sxn;
+      if (tid < BM) sxs[stage * BM + tid] = sxn;
     }
   };
 
@@ -143,32 +187,31 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(GemmParams p) {
         for (int v = 0; v < 4; ++v) yf[i][j][v] = 0.0f;
   }
 
-  const int fr = lane & 15, fk = 16 * (lane >> 4);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint8_t* As = smem + s * kStageBytes + (wm * 64 + fr) * LROW + fk;
-    const uint8_t* Bs = smem + s * kStageBytes + TILE + (wn * 64 + fr) * LROW + fk;
+  // fragment reads: lane (fr, g) takes chunk g + 4h of rows fr + 16 i; the
+  // chunk swizzle depends on fr only (row bits 0-3), so h = 1 is h = 0 ^ 64
+  const int fr = lane & 15;
+  const int foff = fr * LROW + (((lane >> 4) ^ lds_swz(fr)) << 4);
+  auto compute = [&](int stage) {
+    const uint8_t* As = smem + stage * STAGE + wm * 64 * LROW;
+    const uint8_t* Bs = smem + stage * STAGE + ATILE + wn * 64 * LROW;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      v4i a[4], b[4];
+      const int off = foff ^ (64 * h);
+      v4i b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v4i*>(As + i * 16 * LROW + 64 * h);
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + off);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + 64 * h);
+      for (int i = 0; i < 4; ++i) {
+        const v4i a = *reinterpret_cast<const v4i*>(As + i * 16 * LROW + off);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
+      }
     }
     if constexpr (ASYM) {
       // one group of 128 per K step: fold 16*A_g into the float sums
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 sx = *reinterpret_cast<const float4*>(sxs + s * 128 + wm * 64 + 16 * i + 4 * (lane >> 4));
+        const float4 sx = *reinterpret_cast<const float4*>(sxs + stage * BM + wm * 64 + 16 * i + 4 * (lane >> 4));
         const float sv[4] = {sx.x, sx.y, sx.z, sx.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -178,9 +221,46 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(GemmParams p) {
         }
       }
     }
-    if (kt + 1 < nkt) lstore(s ^ 1);
+  };
+
+  // Interleave the widening of the next step (VALU + LDS writes) with this
+  // step's MFMAs: at most about one VALU op per MFMA keeps the matrix core fed
+  // (measured on gfx950: one VALU op per 16x16x64 MFMA is free, two halve
+  // the MFMA rate).  Fragment reads for the first half-step go first.
+  auto schedule = [&]() {
+    if constexpr (!ASYM) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);                              // VALU
+        if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // DS read (h = 1)
+        if (m >= 16 && (m & 1) == 0 && m < 16 + 2 * 2 * NCH) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+    }
+  };
+
+  // prologue: steps 0 and 1 in flight, step 0 in LDS
+  gload(g0, z0, sx0, 0);
+  gload(g1, z1, sx1, 1);
+  lstore(g0, z0, sx0, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nkt; kt += 2) {
+    gload(g0, z0, sx0, kt + 2);       // step kt+2 (past the end: harmless, unused)
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the MFMAs
+    compute(0);                       // step kt
+    lstore(g1, z1, sx1, 1);           // step kt+1
+    schedule();
+    __syncthreads();
+    gload(g1, z1, sx1, kt + 3);       // step kt+3
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);                       // step kt+1
+    lstore(g0, z0, sx0, 0);           // step kt+2 (unused past the end)
+    schedule();
     __syncthreads();
   }
+  if (nkt & 1) compute(0);            // last step of an odd count sits in stage 0
 
   // epilogue: lane holds rows 4*(lane/16)+v, column lane%16 of every 16x16 block
 #pragma unroll
@@ -208,10 +288,177 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(GemmParams p) {
   }
 }
 
+template <int BM>
+constexpr int gemm_lds_bytes() { return 2 * (BM + BN) * LROW + 2 * BM * 4; }
+
+// ---------------------------------------------------------------- A-direct kernel (symmetric)
+// BM x 128 output tile per workgroup, NW waves stacked along M, each wave
+// 16*TM rows x 128 columns (TM x 8 MFMA blocks of 16x16).  gfx950's LDS
+// writes are about three times slower per byte than its 16-byte reads, so
+// only B (the 128 weight rows shared by every wave) is staged in LDS as
+// int8; each wave streams its own A rows straight from global memory into
+// registers (16 packed bytes per lane and row block per K step, two steps
+// ahead) and widens them there.  K-order convention shared by both operands:
+// the packed 16-byte chunk g of a 128-wide K step widens to int8 fragments
+// (g, h = 0) = [lo0 hi0 lo1 hi1] and (g, h = 1) = [lo2 hi2 lo3 hi3].
+template <int NW, int TM, int WPE>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p) {
+  constexpr int BMD = NW * 16 * TM;
+  constexpr int NT = NW * 64;
+  constexpr int NCB = NT >= 512 ? 1 : 512 / NT;  // B chunks (16 packed bytes) per thread per K step
+  const bool b_stager = NT <= 512 || threadIdx.x < 512;   // with 1024 threads, half of them stage B
+  constexpr int BSTAGE = 128 * LROW;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = tm * BMD, n0 = tn * BN;
+  const int nkt = p.K / BK;
+  const int64_t ldc = p.K / 2;
+
+  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
+
+  const int fr = lane & 15, g = lane >> 4;
+  // A: lane (fr, g) of row block i reads packed chunk g of row wave*16*TM + 16 i + fr
+  const int a_off = (wave * 16 * TM + fr) * (int)ldc + 16 * g;
+  // B staging: chunk cb = tid + NT * j -> row cb >> 2, packed chunk cb & 3
+  int b_off[NCB], b_lds[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = tid + NT * j;
+    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
+    b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
+  }
+  // B fragment (g, h) of column block j: int8 chunk 2 g + h of row 16 j + fr
+  const int bf0 = lds_chunk(fr, 2 * g), bf1 = lds_chunk(fr, 2 * g + 1);
+
+  uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
+  auto load_a = [&](uint4* pa, int kt) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
+  };
+  auto load_b = [&](uint4* pb, int kt) {
+    if (!b_stager) return;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4* pb, int stage) {
+    if (!b_stager) return;
+    uint8_t* base = smem + stage * BSTAGE;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+      *reinterpret_cast<uint4*>(base + b_lds[j]) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(base + (b_lds[j] ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  };
+
+  v4i acc[TM][8];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  auto compute = [&](const uint4* pa, int stage) {
+    v4i a[TM][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint32_t w[4] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+      a[i][0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      a[i][1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+    }
+    const uint8_t* Bs = smem + stage * BSTAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const v4i b = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + (h ? bf1 : bf0));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][j] = mfma16(a[i][h], b, acc[i][j]);
+      }
+    }
+  };
+
+  // prologue: A steps 0,1 and B steps 0,1 in flight; B step 0 in LDS
+  load_a(pa0, 0);
+  load_b(pb0, 0);
+  load_a(pa1, 1);
+  load_b(pb1, 1);
+  store_b(pb0, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nkt; kt += 2) {
+    load_b(pb0, kt + 2);              // B step kt+2 (past the end: zeros / unused)
+    compute(pa0, 0);                  // step kt (A from registers, B from stage 0)
+    load_a(pa0, kt + 2);
+    store_b(pb1, 1);                  // B step kt+1
+    __syncthreads();
+    load_b(pb1, kt + 3);
+    compute(pa1, 1);                  // step kt+1
+    load_a(pa1, kt + 3);
+    store_b(pb0, 0);                  // B step kt+2
+    __syncthreads();
+  }
+  if (nkt & 1) compute(pa0, 0);
+
+  // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
+  // block; after dequantizing, a quad transpose gives each lane 4 consecutive
+  // columns of one row, stored as one 16-byte write.
+  const int k4 = fr & 3;
+  const bool vec_ok = (p.ldy & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t rb = m0 + wave * 16 * TM + 16 * i + 4 * g;
+    float sx[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sx[v] = (rb + v < p.M) ? p.xs[rb + v] : 0.0f;
+    const int64_t row = rb + k4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t col = n0 + 16 * j + fr;
+      const float sw = col < p.N ? p.ws[col] : 0.0f;
+      float y[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) y[v] = (sx[v] * sw) * (float)(acc[i][j][v] >> 8);
+      quad_transpose4(y, k4);
+      const int64_t c0 = n0 + 16 * j + (fr & ~3);     // this lane now holds row `row`, columns c0..c0+3
+      if (row < p.M) {
+        float* dst = p.y + row * p.ldy + c0;
+        if (vec_ok && c0 + 3 < p.N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (c0 + c < p.N) dst[c] = y[c];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode kernel
 // M <= 16 rows (symmetric): one workgroup per 16 output columns; the 4 waves
-// split the K steps and stream W's packed rows straight into registers, one
-// 16x16x64 MFMA pair per 128-wide K step (rows of X beyond M are zero).
+// split the 128-wide K steps (wave w takes steps w, w+4, ...).  The kernel
+// is bound by streaming W's packed rows, so every lane issues the loads of 8
+// K steps at once (128 bytes of W in flight per lane, the whole 16-row slab
+// of W per workgroup for K = 4096) before widening them and running one
+// 16x16x64 MFMA pair per step.  Rows of X beyond M and steps beyond K read
+// as zero through the buffer range check.
 __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmParams p) {
   __shared__ v4i red[3][64];
   const int tid = threadIdx.x;
@@ -219,28 +466,39 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmParams p) {
   const int i = lane & 15, kg = 16 * (lane >> 4);
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nkt = p.K / BK;
-  const int64_t ldc = p.K / 2;
-  const bool xv = i < p.M, wv = n0 + i < p.N;
-  const uint8_t* xp = p.xq + (xv ? i : 0) * ldc + kg;
-  const uint8_t* wp = p.wq + (wv ? (n0 + i) : 0) * ldc + kg;
+  const int ldc = p.K / 2;
+  const int64_t nw = p.N - n0 < 16 ? p.N - n0 : 16;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.xq, (short)0, (int)(p.M * ldc), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(nw * ldc), 0x00020000);
+  const int lane_off = i * ldc + kg;
 
   v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll 4
-  for (int kt = wave; kt < nkt; kt += 4) {
-    const uint4 xa = xv ? *reinterpret_cast<const uint4*>(xp + kt * 64) : make_uint4(0u, 0u, 0u, 0u);
-    const uint4 wb = wv ? *reinterpret_cast<const uint4*>(wp + kt * 64) : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
-    const uint32_t ww[4] = {wb.x, wb.y, wb.z, wb.w};
-    uint32_t ao[8], bo[8];
+  for (int t0 = 0; 4 * t0 < nkt; t0 += 8) {
+    uint4 xa[8], wb[8];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      widen_signed(xw[d], ao[2 * d], ao[2 * d + 1]);
-      widen_signed(ww[d], bo[2 * d], bo[2 * d + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int kt = wave + 4 * (t0 + u);
+      const int off = kt < nkt ? lane_off + kt * 64 : 0x7FFFFFF0;
+      wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
     }
-    acc = mfma16(v4i{(int)ao[0], (int)ao[1], (int)ao[2], (int)ao[3]},
-                 v4i{(int)bo[0], (int)bo[1], (int)bo[2], (int)bo[3]}, acc);
-    acc = mfma16(v4i{(int)ao[4], (int)ao[5], (int)ao[6], (int)ao[7]},
-                 v4i{(int)bo[4], (int)bo[5], (int)bo[6], (int)bo[7]}, acc);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t xw[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w};
+      const uint32_t ww[4] = {wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+      uint32_t ao[8], bo[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        widen_signed(xw[d], ao[2 * d], ao[2 * d + 1]);
+        widen_signed(ww[d], bo[2 * d], bo[2 * d + 1]);
+      }
+      acc = mfma16(v4i{(int)ao[0], (int)ao[1], (int)ao[2], (int)ao[3]},
+                   v4i{(int)bo[0], (int)bo[1], (int)bo[2], (int)bo[3]}, acc);
+      acc = mfma16(v4i{(int)ao[4], (int)ao[5], (int)ao[6], (int)ao[7]},
+                   v4i{(int)bo[4], (int)bo[5], (int)bo[6], (int)bo[7]}, acc);
+    }
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
@@ -261,12 +519,9 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmParams p) {
 }
 
 hipError_t gemm_prepare_device() {
-  // The tiled kernel uses more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB).
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+  // The asymmetric tiled kernel uses more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB).
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<128, true>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<128>());
 }
 
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
@@ -276,11 +531,26 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     hipLaunchKernelGGL(gemm_decode_kernel, dim3((uint32_t)grid), dim3(256), 0, st, p);
     return hipGetLastError();
   }
-  const int64_t grid = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  if (mode == kModeSym)
-    hipLaunchKernelGGL(gemm_tile_kernel<false>, dim3((uint32_t)grid), dim3(256), kGemmLds, st, p);
-  else
-    hipLaunchKernelGGL(gemm_tile_kernel<true>, dim3((uint32_t)grid), dim3(256), kGemmLds, st, p);
+  if (mode == kModeSym) {
+    // A-direct kernel.  Large M: 256-row tiles of 8 waves (32 x 128 each) when
+    // there are at least two tiles per CU (two workgroups share a CU), else
+    // 256-row tiles of 16 waves (16 x 128 each) so that one workgroup per CU
+    // still has four waves per SIMD.  M <= 512: 64-row tiles of 4 waves.
+    if (p.M > 512) {
+      const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
+      if (grid >= 512)
+        hipLaunchKernelGGL((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_adirect_kernel<16, 1, 4>), dim3((uint32_t)grid), dim3(1024), 0, st, p);
+    } else {
+      const int64_t grid = ((p.M + 63) / 64) * ((p.N + BN - 1) / BN);
+      hipLaunchKernelGGL((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
+    }
+    return hipGetLastError();
+  }
+  // asymmetric per-group activations: 128-row tiles with int8 A and B in LDS
+  const int64_t grid = ((p.M + 127) / 128) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_tile_kernel<128, true>), dim3((uint32_t)grid), dim3(256), gemm_lds_bytes<128>(), st, p);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct RQParams {
   int32_t nb;        // K / 128 (set by the launcher)
   int32_t seg;       // threads per row slot (set by the launcher)
   int32_t rows_per_wg;
+  int32_t log2seg;   // log2(seg) when rows_per_wg > 1
   float cdiv;        // fl32(7 sqrt(b)) (sym) or fl32(15 sqrt(b)) (asym)
 };
 

@@ -114,150 +114,179 @@ template <int MODE, int LOG_NB_FULL, bool GSUM, bool STRIDED>
 __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
-  const int slot = tid / p.seg;
+  const int slot = p.rows_per_wg == 1 ? 0 : tid >> p.log2seg;
   const int lt = tid - slot * p.seg;
-  const int64_t row = (int64_t)blockIdx.x * p.rows_per_wg + slot;
   const int blk = lt >> 2;
   const int q = lt & 3;
-  const bool valid = (row < p.rows) && (blk < p.nb);
+  const bool lane_ok = blk < p.nb;
+  // cross-lane butterfly coefficients and the sign they leave on this lane
+  const float s0 = (q & 1) ? -1.0f : 1.0f;
+  const float s1 = (q & 2) ? -1.0f : 1.0f;
+  const float sgn = ((q ^ (q >> 1)) & 1) ? -1.0f : 1.0f;
+  // byte offset of this lane's first chunk inside its row group (dense rows);
+  // padding lanes read past the buffer's end and get zeros
+  const uint32_t lane_off = lane_ok ? (uint32_t)(((int64_t)slot * p.ss + blk * 128 + q * 8) * 2) : 0x7FFFFFF0u;
+  const int64_t ngroups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
 
-  int64_t roff;
-  if constexpr (STRIDED) {
-    const uint32_t r = (uint32_t)row;
-    const uint32_t s = r % p.S, t = r / p.S;
-    const uint32_t h = t % p.H, b = t / p.H;
-    roff = (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)s * p.ss;
-  } else {
-    roff = row * p.ss;
-  }
+  for (int64_t rgi = blockIdx.x; rgi < ngroups; rgi += gridDim.x) {
+    const int64_t row0 = rgi * p.rows_per_wg;
+    const int64_t row = row0 + slot;
+    const bool valid = lane_ok && row < p.rows;
 
-  // ---- load 32 fp16 values: chunks q, q+4, q+8, q+12 of block `blk`
-  float v[32];
-  {
-    const uint16_t* src = p.x + roff + blk * 128 + q * 8;
+    // ---- load 32 fp16 values (chunks q, q+4, q+8, q+12 of block `blk`)
     uint4 w[4];
+    if constexpr (STRIDED) {
+      const uint32_t r = (uint32_t)row;
+      const uint32_t s = r % p.S, t = r / p.S;
+      const uint32_t h = t % p.H, b = t / p.H;
+      const uint16_t* src = p.x + (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)s * p.ss + blk * 128 + q * 8;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      w[r] = valid ? *reinterpret_cast<const uint4*>(src + 32 * r) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t d[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * r + 2 * j] = h2f(d[j] & 0xFFFFu);
-        v[8 * r + 2 * j + 1] = h2f(d[j] >> 16);
-      }
-    }
-  }
-
-  // ---- 128-point FWHT: 5 register bits, then the 2 quad-lane bits by DPP
-  fwht_regs<5>(v);
-  {
-    const float s0 = (q & 1) ? -1.0f : 1.0f;   // high half of the pair keeps partner - self
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = fmaf(v[i], s0, dpp_f<0xB1>(v[i]));
-    const float s1 = (q & 2) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = fmaf(v[i], s1, dpp_f<0x4E>(v[i]));
-  }
-
-  // ---- full width: butterflies over the block index through LDS
-  if constexpr (LOG_NB_FULL > 0) {
-    float* buf = lds + (size_t)slot * p.K;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(buf + blk * 128 + 32 * r + 8 * q);
-      dst[0] = make_float4(v[8 * r + 0], v[8 * r + 1], v[8 * r + 2], v[8 * r + 3]);
-      dst[1] = make_float4(v[8 * r + 4], v[8 * r + 5], v[8 * r + 6], v[8 * r + 7]);
-    }
-    __syncthreads();
-    fwht_block_axis<LOG_NB_FULL>(buf, lt);
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4* s4 = reinterpret_cast<const float4*>(buf + blk * 128 + 32 * r + 8 * q);
-      const float4 a = s4[0], b = s4[1];
-      v[8 * r + 0] = a.x; v[8 * r + 1] = a.y; v[8 * r + 2] = a.z; v[8 * r + 3] = a.w;
-      v[8 * r + 4] = b.x; v[8 * r + 5] = b.y; v[8 * r + 6] = b.z; v[8 * r + 7] = b.w;
-    }
-    __syncthreads();   // the row buffer is reused for the reduction below
-  }
-
-  const int64_t crow = row * (int64_t)(p.K / 2);
-  uint32_t words[4];
-
-  if constexpr (MODE == kModeSym) {
-    // ---- per-row absmax
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
-    am = quad_max(am);
-    if (p.seg <= kWave) {
-      for (int m = 4; m < p.seg; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+      for (int r4 = 0; r4 < 4; ++r4)
+        w[r4] = valid ? *reinterpret_cast<const uint4*>(src + 32 * r4) : make_uint4(0u, 0u, 0u, 0u);
     } else {
-      for (int m = 4; m < kWave; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
-      float* red = lds;
-      const int nw = p.seg / kWave;
-      if ((lt & (kWave - 1)) == 0) red[slot * 16 + (lt / kWave)] = am;
+      const int64_t nrows = p.rows - row0 < p.rows_per_wg ? p.rows - row0 : p.rows_per_wg;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.x + row0 * p.ss), (short)0, (int)(nrows * p.ss * 2), 0x00020000);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        w[r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_off, 64 * r4, 0));
+    }
+
+    // the first butterfly (element bit 0: the two halves of a dword) is fused
+    // with the conversion to fp32
+    float v[32];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t d[4] = {w[r4].x, w[r4].y, w[r4].z, w[r4].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cvt_bfly(d[j], v[8 * r4 + 2 * j], v[8 * r4 + 2 * j + 1]);
+    }
+    // remaining register bits (element bits 1-2, 5-6) ...
+#pragma unroll
+    for (int b = 2; b < 32; b <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (!(i & b)) {
+          const float a = v[i], c = v[i | b];
+          v[i] = a + c;
+          v[i | b] = a - c;
+        }
+      }
+    }
+    // ... and the two quad-lane bits (element bits 3-4): afterwards this lane
+    // holds sgn * z
+    dpp_bfly_q0(v, s0);
+    dpp_bfly_q0(v + 16, s0);
+    dpp_bfly_q1(v, s1);
+    dpp_bfly_q1(v + 16, s1);
+
+    // ---- full width: butterflies over the block index through LDS.  Values
+    // at one in-block position share their sign, so the signed values
+    // transform linearly and keep it.
+    if constexpr (LOG_NB_FULL > 0) {
+      float* buf = lds + (size_t)slot * p.K;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4* dst = reinterpret_cast<float4*>(buf + blk * 128 + 32 * r4 + 8 * q);
+        dst[0] = make_float4(v[8 * r4 + 0], v[8 * r4 + 1], v[8 * r4 + 2], v[8 * r4 + 3]);
+        dst[1] = make_float4(v[8 * r4 + 4], v[8 * r4 + 5], v[8 * r4 + 6], v[8 * r4 + 7]);
+      }
       __syncthreads();
-      am = 0.0f;
-      for (int w = 0; w < nw; ++w) am = fmaxf(am, red[slot * 16 + w]);
-    }
-    const float inv = am > 0.0f ? div_rn(7.0f, am) : 0.0f;
-    // codes: fma gives 2^23*1.5 + 8 + rne(z*inv); the low nibble is the code
-    // in offset-8 binary, turned into two's complement by the final xor.
-    int gs = 0;
+      fwht_block_axis<LOG_NB_FULL>(buf, lt);
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t b[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        b[e] = fbits(fmaf(v[8 * r + e], inv, kRneMagic + 8.0f));
-        if constexpr (GSUM) gs += (int)(b[e] - (kRneMagicBits + 8u));
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4* s4 = reinterpret_cast<const float4*>(buf + blk * 128 + 32 * r4 + 8 * q);
+        const float4 a = s4[0], b = s4[1];
+        v[8 * r4 + 0] = a.x; v[8 * r4 + 1] = a.y; v[8 * r4 + 2] = a.z; v[8 * r4 + 3] = a.w;
+        v[8 * r4 + 4] = b.x; v[8 * r4 + 5] = b.y; v[8 * r4 + 6] = b.z; v[8 * r4 + 7] = b.w;
       }
-      words[r] = pack8(b) ^ 0x88888888u;
+      __syncthreads();   // the row buffer is reused for the reduction below
     }
-    if (valid) {
+
+    const int64_t crow = row * (int64_t)(p.K / 2);
+    uint32_t words[4];
+
+    if constexpr (MODE == kModeSym) {
+      // ---- per-row absmax
+      float am = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r + 4 * q) = words[r];
-      if (lt == 0) p.scales[row] = am > 0.0f ? div_rn(am, p.cdiv) : 0.0f;
-    }
-    if constexpr (GSUM) {
-      gs = quad_sum(gs);
-      if (valid && q == 0) p.gsum[row * p.nb + blk] = gs;
-    }
-  } else {
-    // ---- asymmetric, one group per 128-block
-    float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      lo = fminf(lo, v[i]);
-      hi = fmaxf(hi, v[i]);
-    }
-    lo = quad_min(lo);
-    hi = quad_max(hi);
-    const float rg = hi - lo;
-    const float inv = rg > 0.0f ? div_rn(15.0f, rg) : 0.0f;
-    int zp = (int)(fbits(fmaf(-lo, inv, kRneMagic)) - kRneMagicBits);
-    zp = zp < 0 ? 0 : (zp > 15 ? 15 : zp);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t b[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t u = fbits(fmaf(v[8 * r + e], inv, kRneMagic)) + (uint32_t)zp;
-        b[e] = u < kRneMagicBits + 15u ? u : kRneMagicBits + 15u;
+      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+      am = quad_max(am);
+      if (p.seg <= kWave) {
+        for (int m = 4; m < p.seg; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+      } else {
+        for (int m = 4; m < kWave; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+        float* red = lds;
+        const int nw = p.seg / kWave;
+        if ((lt & (kWave - 1)) == 0) red[slot * 16 + (lt / kWave)] = am;
+        __syncthreads();
+        am = 0.0f;
+        for (int w2 = 0; w2 < nw; ++w2) am = fmaxf(am, red[slot * 16 + w2]);
+        __syncthreads();   // red is rewritten by the next row group
       }
-      words[r] = pack8(b);
-    }
-    if (valid) {
+      const float inv = am > 0.0f ? div_rn(7.0f, am) : 0.0f;
+      const float sinv = sgn * inv;      // (sgn z) * (sgn inv) = z * inv exactly
+      // codes: fma gives 2^23*1.5 + 8 + rne(z*inv); the low nibble is the code
+      // in offset-8 binary, turned into two's complement by the final xor.
+      uint32_t gsb = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r + 4 * q) = words[r];
-      if (q == 0) {
-        p.scales[row * p.nb + blk] = rg > 0.0f ? div_rn(rg, p.cdiv) : 0.0f;
-        p.zeros[row * p.nb + blk] = (uint8_t)zp;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          b[e] = fbits(fmaf(v[8 * r4 + e], sinv, kRneMagic + 8.0f));
+          if constexpr (GSUM) gsb += b[e];
+        }
+        words[r4] = pack8(b) ^ 0x88888888u;
+      }
+      if (valid) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r4 + 4 * q) = words[r4];
+        if (lt == 0) p.scales[row] = am > 0.0f ? div_rn(am, p.cdiv) : 0.0f;
+      }
+      if constexpr (GSUM) {
+        // sum of the 32 codes: the bit patterns are magic + 8 + code
+        const int gs = quad_sum((int)(gsb - 32u * (kRneMagicBits + 8u)));
+        if (valid && q == 0) p.gsum[row * p.nb + blk] = gs;
+      }
+    } else {
+      // ---- asymmetric, one group per 128-block
+      float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        mn = fminf(mn, v[i]);
+        mx = fmaxf(mx, v[i]);
+      }
+      // this lane holds sgn * z: the range of z is [mn, mx] or [-mx, -mn]
+      float lo = sgn > 0.0f ? mn : -mx;
+      float hi = sgn > 0.0f ? mx : -mn;
+      lo = quad_min(lo);
+      hi = quad_max(hi);
+      const float rg = hi - lo;
+      const float inv = rg > 0.0f ? div_rn(15.0f, rg) : 0.0f;
+      const float sinv = sgn * inv;
+      int zp = (int)(fbits(fmaf(-lo, inv, kRneMagic)) - kRneMagicBits);
+      zp = zp < 0 ? 0 : (zp > 15 ? 15 : zp);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = fbits(fmaf(v[8 * r4 + e], sinv, kRneMagic)) + (uint32_t)zp;
+          b[e] = u < kRneMagicBits + 15u ? u : kRneMagicBits + 15u;
+        }
+        words[r4] = pack8(b);
+      }
+      if (valid) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r4 + 4 * q) = words[r4];
+        if (q == 0) {
+          p.scales[row * p.nb + blk] = rg > 0.0f ? div_rn(rg, p.cdiv) : 0.0f;
+          p.zeros[row * p.nb + blk] = (uint8_t)zp;
+        }
       }
     }
   }
@@ -304,7 +333,11 @@ RQGeometry rq_geometry(int64_t rows, int K) {
     g.rows_per_wg = g.seg >= 256 ? 1 : 256 / g.seg;
   }
   g.threads = g.seg * g.rows_per_wg;
-  g.grid = (rows + g.rows_per_wg - 1) / g.rows_per_wg;
+  // row groups are strided over the workgroups: enough of them to fill every
+  // CU several times over, each looping over a few groups
+  const int64_t groups = (rows + g.rows_per_wg - 1) / g.rows_per_wg;
+  const int64_t cap = (int64_t)256 * (2048 / g.threads) * 2;
+  g.grid = groups < cap ? groups : cap;
   return g;
 }
 
@@ -313,6 +346,8 @@ hipError_t launch_rotate_quant(RQParams p, int mode, bool full, bool gsum, bool 
   const RQGeometry g = rq_geometry(p.rows, p.K);
   p.seg = g.seg;
   p.rows_per_wg = g.rows_per_wg;
+  p.log2seg = 0;
+  while ((1 << p.log2seg) < g.seg) ++p.log2seg;   // seg is a power of two whenever rows_per_wg > 1
   p.nb = p.K / 128;
   int logf = 0;
   if (full && p.nb > 1) {

@@ -174,7 +174,8 @@ def _rand_codes(seed, rows, K, lo=-7, hi=7):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (4, 100, 256), (16, 4096, 4096), (17, 257, 1152),
                                    (128, 128, 128), (300, 200, 384), (2048, 512, 4096),
-                                   (129, 130, 14336)])
+                                   (129, 130, 14336), (513, 100, 640), (4096, 4096, 256),
+                                   (2048, 4096, 128)])
 def test_gemm_same_codes_sym_bitexact(M, N, K):
     qa = _rand_codes(M * N + K, M, K)
     qb = _rand_codes(M + N * K, N, K)
