@@ -43,12 +43,6 @@ __device__ __forceinline__ void widen_signed(uint32_t p, uint32_t& even16, uint3
   odd16 = p & 0xF0F0F0F0u;
 }
 
-// Unsigned nibbles u, zero-point z (replicated in every byte as zx4):
-// bytes of the result are the int8 levels u - z.
-__device__ __forceinline__ uint32_t levels(uint32_t u4, uint32_t zx4) {
-  return ((u4 | 0x80808080u) - zx4) ^ 0x80808080u;
-}
-
 __device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
@@ -81,215 +75,6 @@ __device__ __forceinline__ void quad_transpose4(float* y, int k) {
 }
 
 }  // namespace
-
-// ---------------------------------------------------------------- tiled kernel
-// BM x 128 output tile per workgroup (BM = 128 or 256), BM/64 x 2 waves of
-// 64x64 each (4 x 4 MFMA blocks of 16x16).  K advances 128 (one asymmetric
-// group) per step.  Pipeline: while step t's MFMAs run out of one LDS stage,
-// the raw buffer loads of step t+2 are in flight into one register set and
-// step t+1's packed bytes (loaded a step earlier) are widened to int8 and
-// written to the other stage; one barrier per step.  Buffer loads past the
-// end of A or B return zero, so ragged M, N and the prefetch past the last
-// step need no branches in the main loop.
-template <int BM, bool ASYM>
-__global__ void __launch_bounds__(BM * 2)
-__attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2, ASYM ? 1 : 2))) gemm_tile_kernel(GemmParams p) {
-  constexpr int NT = BM * 2;                  // threads: BM/64 x 2 waves
-  constexpr int ROWS = BM + BN;               // operand rows per K step
-  constexpr int NCH = ROWS * 4 / NT;          // 16-byte chunks per thread per K step
-  constexpr int NCA = BM * 4 / NT;            // ... of which from A (the rest from B)
-  constexpr int ATILE = BM * LROW;
-  constexpr int STAGE = ROWS * LROW;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* sxs = reinterpret_cast<float*>(smem + 2 * STAGE);   // asym: [2][BM] row scales / 16
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int nkt = p.K / BK;
-  const int64_t ldc = p.K / 2;   // packed bytes per row
-  const int G = nkt;
-
-  // buffer resources covering rows m0.. of A and n0.. of B (reads past the end give 0)
-  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
-
-  uint4 g0[NCH], g1[NCH];
-  uint32_t z0[NCH], z1[NCH];
-  float sx0 = 0.0f, sx1 = 0.0f;
-  auto gload = [&](uint4* g, uint32_t* z, float& sxn, int kt) {
-    const int kc = kt < nkt ? kt : nkt - 1;       // clamped index for the side arrays
-    // chunk j < NCA comes from A, the others from B (ci = tid + NT j runs over
-    // the BM A rows first, then the 128 B rows)
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + NT * j;
-      const int row = ci >> 2, c = ci & 3;
-      if (j < NCA) {
-        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            ra, row * (int)ldc + 16 * c + kt * 64, 0, 0));
-        if constexpr (ASYM) {
-          const int64_t grow = m0 + row;
-          z[j] = grow < p.M ? (uint32_t)p.xz[grow * G + kc] * 0x01010101u : 0u;
-        }
-      } else {
-        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            rb, (row - BM) * (int)ldc + 16 * c + kt * 64, 0, 0));
-      }
-    }
-    if constexpr (ASYM) sxn = (tid < BM && m0 + tid < p.M) ? p.xs[(m0 + tid) * G + kc] * 0.0625f : 0.0f;
-  };
-  auto lstore = [&](const uint4* g, const uint32_t* z, float sxn, int stage) {
-    uint8_t* base = smem + stage * STAGE;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + NT * j;
-      const uint32_t w[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
-      uint32_t o[8];
-      if (ASYM && j < NCA) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          o[2 * d] = levels(w[d] & 0x0F0F0F0Fu, z[j]);
-          o[2 * d + 1] = levels((w[d] >> 4) & 0x0F0F0F0Fu, z[j]);
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
-      }
-      const int row = ci >> 2, c = 2 * (ci & 3);
-      *reinterpret_cast<uint4*>(base + lds_chunk(row, c)) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(base + lds_chunk(row, c + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-    if constexpr (ASYM) {
-      if (tid < BM) sxs[stage * BM + tid] = sxn;
-    }
-  };
-
-  v4i acc[4][4];
-  float yf[ASYM ? 4 : 1][ASYM ? 4 : 1][ASYM ? 4 : 1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-  if constexpr (ASYM) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) yf[i][j][v] = 0.0f;
-  }
-
-  // fragment reads: lane (fr, g) takes chunk g + 4h of rows fr + 16 i; the
-  // chunk swizzle depends on fr only (row bits 0-3), so h = 1 is h = 0 ^ 64
-  const int fr = lane & 15;
-  const int foff = fr * LROW + (((lane >> 4) ^ lds_swz(fr)) << 4);
-  auto compute = [&](int stage) {
-    const uint8_t* As = smem + stage * STAGE + wm * 64 * LROW;
-    const uint8_t* Bs = smem + stage * STAGE + ATILE + wn * 64 * LROW;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int off = foff ^ (64 * h);
-      v4i b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + off);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i a = *reinterpret_cast<const v4i*>(As + i * 16 * LROW + off);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a, b[j], acc[i][j]);
-      }
-    }
-    if constexpr (ASYM) {
-      // one group of 128 per K step: fold 16*A_g into the float sums
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 sx = *reinterpret_cast<const float4*>(sxs + stage * BM + wm * 64 + 16 * i + 4 * (lane >> 4));
-        const float sv[4] = {sx.x, sx.y, sx.z, sx.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sv[v], (float)acc[i][j][v], yf[i][j][v]);
-          acc[i][j] = v4i{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-
-  // Interleave the widening of the next step (VALU + LDS writes) with this
-  // step's MFMAs: at most about one VALU op per MFMA keeps the matrix core fed
-  // (measured on gfx950: one VALU op per 16x16x64 MFMA is free, two halve
-  // the MFMA rate).  Fragment reads for the first half-step go first.
-  auto schedule = [&]() {
-    if constexpr (!ASYM) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);                              // VALU
-        if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // DS read (h = 1)
-        if (m >= 16 && (m & 1) == 0 && m < 16 + 2 * 2 * NCH) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-    }
-  };
-
-  // prologue: steps 0 and 1 in flight, step 0 in LDS
-  gload(g0, z0, sx0, 0);
-  gload(g1, z1, sx1, 1);
-  lstore(g0, z0, sx0, 0);
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nkt; kt += 2) {
-    gload(g0, z0, sx0, kt + 2);       // step kt+2 (past the end: harmless, unused)
-    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the MFMAs
-    compute(0);                       // step kt
-    lstore(g1, z1, sx1, 1);           // step kt+1
-    schedule();
-    __syncthreads();
-    gload(g1, z1, sx1, kt + 3);       // step kt+3
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);                       // step kt+1
-    lstore(g0, z0, sx0, 0);           // step kt+2 (unused past the end)
-    schedule();
-    __syncthreads();
-  }
-  if (nkt & 1) compute(0);            // last step of an odd count sits in stage 0
-
-  // epilogue: lane holds rows 4*(lane/16)+v, column lane%16 of every 16x16 block
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t rb = m0 + wm * 64 + 16 * i + 4 * (lane >> 4);
-    float sx[4];
-    if constexpr (!ASYM) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sx[v] = (rb + v < p.M) ? p.xs[rb + v] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 64 + 16 * j + fr;
-      if (col >= p.N) continue;
-      const float sw = p.ws[col];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (rb + v >= p.M) continue;
-        float y;
-        if constexpr (ASYM) y = yf[i][j][v] * sw;
-        else y = (sx[v] * sw) * (float)(acc[i][j][v] >> 8);
-        p.y[(rb + v) * p.ldy + col] = y;
-      }
-    }
-  }
-}
-
-template <int BM>
-constexpr int gemm_lds_bytes() { return 2 * (BM + BN) * LROW + 2 * BM * 4; }
 
 // ---------------------------------------------------------------- A-direct kernel (symmetric)
 // BM x 128 output tile per workgroup, NW waves stacked along M, each wave
@@ -451,6 +236,187 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
   }
 }
 
+// ---------------------------------------------------------------- A-direct kernel (asymmetric)
+// Same tiling and K-order convention as the symmetric A-direct kernel.
+// Activation codes are unsigned with one zero-point per (row, group of 128);
+// each wave widens its A rows straight to the int8 levels u - zp (|u - zp| <=
+// 15), so the MFMA accumulates 16 * A_g exactly; at the end of every K step
+// (= one group) the group sum is folded into fp32 with that row's scale / 16.
+template <int NW, int TM, int WPE>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int NCB = NT >= 512 ? 1 : 512 / NT;
+  constexpr int BSTAGE = 128 * LROW;
+  constexpr int BMD = NW * 16 * TM;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
+  const bool b_stager = NT <= 512 || threadIdx.x < 512;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = tm * BMD, n0 = tn * BN;
+  const int nkt = p.K / BK;
+  const int G = nkt;
+  const int64_t ldc = p.K / 2;
+
+  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
+
+  const int fr = lane & 15, g = lane >> 4;
+  const int a_off = (wave * 16 * TM + fr) * (int)ldc + 16 * g;
+  int b_off[NCB], b_lds[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = tid + NT * j;
+    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
+    b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
+  }
+  const int bf0 = lds_chunk(fr, 2 * g), bf1 = lds_chunk(fr, 2 * g + 1);
+
+  // per-lane row bookkeeping: the A row a lane widens (zero-point) and the
+  // four C rows it accumulates (scales)
+  int64_t arow[TM], crow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    arow[i] = m0 + wave * 16 * TM + 16 * i + fr;
+    crow[i] = m0 + wave * 16 * TM + 16 * i + 4 * g;
+  }
+
+  // A codes, zero-points and the C rows' scales (/ 16) of a K step travel
+  // together, two steps ahead of their use
+  uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
+  uint32_t z0[TM], z1[TM];
+  float s0[TM][4], s1[TM][4];
+  auto load_a = [&](uint4* pa, uint32_t* z, float (*sx)[4], int kt) {
+    const int kc = kt < nkt ? kt : nkt - 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
+      z[i] = arow[i] < p.M ? (uint32_t)p.xz[arow[i] * G + kc] : 0u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sx[i][v] = crow[i] + v < p.M ? p.xs[(crow[i] + v) * G + kc] * 0.0625f : 0.0f;
+    }
+  };
+  auto load_b = [&](uint4* pb, int kt) {
+    if (!b_stager) return;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4* pb, int stage) {
+    if (!b_stager) return;
+    uint8_t* base = smem + stage * BSTAGE;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+      *reinterpret_cast<uint4*>(base + b_lds[j]) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(base + (b_lds[j] ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  };
+
+  v4i acc[TM][8];
+  float yf[TM][8][4];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[i][j] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yf[i][j][v] = 0.0f;
+    }
+
+  auto compute = [&](const uint4* pa, const uint32_t* z, const float (*sx)[4], int stage) {
+    v4i a[TM][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
+      const uint32_t bias = (128u - z[i]) * 0x01010101u;
+      const uint32_t w[4] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        o[2 * d] = ((w[d] & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+        o[2 * d + 1] = (((w[d] >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+      }
+      a[i][0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      a[i][1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+    }
+    const uint8_t* Bs = smem + stage * BSTAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const v4i b = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + (h ? bf1 : bf0));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)   // a group starts from zero: no separate reset
+          acc[i][j] = mfma16(a[i][h], b, h ? acc[i][j] : v4i{0, 0, 0, 0});
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sx[i][v], (float)acc[i][j][v], yf[i][j][v]);
+  };
+
+  load_a(pa0, z0, s0, 0);
+  load_b(pb0, 0);
+  load_a(pa1, z1, s1, 1);
+  load_b(pb1, 1);
+  store_b(pb0, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nkt; kt += 2) {
+    load_b(pb0, kt + 2);
+    compute(pa0, z0, s0, 0);
+    load_a(pa0, z0, s0, kt + 2);
+    store_b(pb1, 1);
+    __syncthreads();
+    load_b(pb1, kt + 3);
+    compute(pa1, z1, s1, 1);
+    load_a(pa1, z1, s1, kt + 3);
+    store_b(pb0, 0);
+    __syncthreads();
+  }
+  if (nkt & 1) compute(pa0, z0, s0, 0);
+
+  const int k4 = fr & 3;
+  const bool vec_ok = (p.ldy & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = crow[i] + k4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t col = n0 + 16 * j + fr;
+      const float sw = col < p.N ? p.ws[col] : 0.0f;
+      float y[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) y[v] = yf[i][j][v] * sw;
+      quad_transpose4(y, k4);
+      const int64_t c0 = n0 + 16 * j + (fr & ~3);
+      if (row < p.M) {
+        float* dst = p.y + row * p.ldy + c0;
+        if (vec_ok && c0 + 3 < p.N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (c0 + c < p.N) dst[c] = y[c];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode kernel
 // M <= 16 rows (symmetric): one workgroup per 16 output columns; the 4 waves
 // split the 128-wide K steps (wave w takes steps w, w+4, ...).  The kernel
@@ -518,11 +484,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(GemmParams p) {
   }
 }
 
-hipError_t gemm_prepare_device() {
-  // The asymmetric tiled kernel uses more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB).
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<128, true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<128>());
-}
+hipError_t gemm_prepare_device() { return hipSuccess; }   // no per-device setup needed
 
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
   if (p.M == 0) return hipSuccess;
@@ -548,9 +510,10 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  // asymmetric per-group activations: 128-row tiles with int8 A and B in LDS
+  // asymmetric per-group activations: 128-row tiles of 8 waves (16 x 128 each);
+  // the per-group fp32 fold needs the registers of a wider wave tile
   const int64_t grid = ((p.M + 127) / 128) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tile_kernel<128, true>), dim3((uint32_t)grid), dim3(256), gemm_lds_bytes<128>(), st, p);
+  hipLaunchKernelGGL((gemm_adirect_asym_kernel<8, 1, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
