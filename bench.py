@@ -6,12 +6,19 @@ outlier channels x30), W 4096x4096 fp16 ~N(0, 0.02), 128-wide Hadamard
 blocks (--had full: one 4096-point Hadamard), symmetric INT4 per token and
 per output channel.  Synthetic, seeded inputs from `workloads`.
 
-One step = one pass of the whole path over one batch:
-    quant_weight_offline(W)  -> rotate_quant_act(X)  -> w4a4_gemm
+One step = one pass of the whole path over one batch, on one HIP stream:
+    quant_weight_offline(W) -> rotate_quant_act(X) -> w4a4_gemm
 Inputs sit in HBM before the timed region; 8 copies of the inputs and
 outputs are cycled so that a step never finds its operands in the 256 MiB
-last-level cache.  Every kernel is bracketed by HIP events on the stream it
-runs on, so the per-kernel averages come from the timed steps themselves.
+last-level cache.  The GEMM launch of every timed step carries a pair of
+HIP events armed through w4a4_time_next_launch: the runtime stamps the
+kernel's own start and end into them, so its average is the device
+duration taken live over the timed steps, with no marker packets between
+kernels.  The two rotate+quantize kernels are timed the same way in a second
+pass after the timed region (arming every launch makes the step host-bound).
+(Running the weight and activation steps on two streams, eagerly or as a
+captured HIP graph, measured slower here: the cross-stream waits and graph
+launches cost more host time than the overlap saves.)
 
 Prints one JSON line; value = 2*M*N*K / step time (TOPS of the whole step).
 `--suite` instead prints one line per kernel and configuration (cold and
@@ -57,55 +64,58 @@ def profile_traffic(kernel_key: str, src: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(reps: int = 3) -> dict:
-    """The CPU oracle on the same q_proj step, timed on this host's cores."""
-    import numpy as np
-
+def cpu_baseline(min_seconds: float = 10.0, min_reps: int = 3) -> dict:
+    """The CPU oracle on the same q_proj step, timed on this host's cores:
+    whole steps repeated until about `min_seconds` of work (at least
+    `min_reps` steps)."""
     import oracle as O
     import workloads as WL
     from threadpoolctl import threadpool_info
 
     d = WL.qproj()
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    times = []
+    while len(times) < min_reps or sum(times) < min_seconds:
+        t0 = time.perf_counter()
         wq = O.quant_weight_offline(d["W"], 128)
         a = O.rotate_quant_act(d["X"], 128, "sym")
         acc = O.int_gemm(a["codes"], wq["codes"])
         O.epilogue_sym_f32(acc, a["scale"], wq["scale"])
-    dt = (time.perf_counter() - t0) / reps
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     M, N, K = 2048, 4096, 4096
     return {"value": round(2 * M * N * K / dt / 1e12, 5), "unit": "TOPS", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"full q_proj step (weight rotate+quant, activation rotate+quant, exact integer "
-                      f"GEMM, fp32 epilogue) at M=2048 N=K=4096, mean of {reps} runs, "
-                      f"{dt:.3f} s per step, numpy float64 + BLAS"}
+            "sample": f"{len(times)} full q_proj steps (weight rotate+quant, activation rotate+quant, exact "
+                      f"integer GEMM, fp32 epilogue) at M=2048 N=K=4096, {dt:.3f} s per step, "
+                      f"{sum(times):.1f} s in all; numpy float64 + BLAS"}
 
 
 def _time_kernel(torch, fn, flush, n=30, warm_n=50):
-    """Median / p10 / p90 of one launch after flushing the caches (cold), and
-    the mean of back-to-back launches (warm)."""
-    stream = torch.cuda.current_stream()
+    """Device duration of the kernel one call of `fn` launches: median / p10 /
+    p90 after flushing the caches (cold), and the mean over back-to-back
+    launches (warm).  Each launch carries its own events through
+    w4a4_time_next_launch, so the figures are kernel durations only."""
+    from rotation_w4a4_quantization_amd.timing import HipEvents
+    hev = HipEvents()
     for _ in range(3):
         fn()
     cold = []
-    for _ in range(n):
+    ev = [hev.pair() for _ in range(max(n, warm_n))]
+    for i in range(n):
         flush()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        hev.arm(*ev[i])
         fn()
-        b.record(stream)
-        b.synchronize()
-        cold.append(a.elapsed_time(b))
+        cold.append(hev.elapsed(*ev[i]))
     cold.sort()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(warm_n):
+    torch.cuda.synchronize()
+    for i in range(warm_n):
+        hev.arm(*ev[i])
         fn()
-    b.record(stream)
-    b.synchronize()
+    warm = sum(hev.elapsed(*e) for e in ev[:warm_n]) / warm_n
+    hev.close()
     return dict(cold_ms_median=cold[len(cold) // 2], cold_ms_p10=cold[len(cold) // 10],
-                cold_ms_p90=cold[(9 * len(cold)) // 10], warm_ms=a.elapsed_time(b) / warm_n)
+                cold_ms_p90=cold[(9 * len(cold)) // 10], warm_ms=warm)
 
 
 def run_suite(torch, R, WL):
@@ -246,8 +256,9 @@ def run_only(torch, R, WL, which, steps, had):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first; a few hundred let the clocks settle")
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
@@ -298,45 +309,63 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     lib = _lib.load()
+    from rotation_w4a4_quantization_amd.timing import HipEvents
+    hev = HipEvents()
+    ptrs = [{k: v.data_ptr() for k, v in s.items()} for s in sets]
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        st = lib.quant_weight_offline(s["w"].data_ptr(), N, K, K, hb, s["wc"].data_ptr(),
-                                      s["ws"].data_ptr(), s["wg"].data_ptr(), sp)
-        if ev is not None:
-            ev[1].record(stream)
-        st |= lib.rotate_quant_act(s["x"].data_ptr(), M, K, K, hb, _lib.W4A4_ACT_SYM_TOKEN,
-                                   s["xc"].data_ptr(), s["xs"].data_ptr(), None, sp)
-        if ev is not None:
-            ev[2].record(stream)
-        st |= lib.w4a4_gemm(s["xc"].data_ptr(), s["xs"].data_ptr(), None, _lib.W4A4_ACT_SYM_TOKEN,
-                            s["wc"].data_ptr(), s["ws"].data_ptr(), None, M, N, K, s["y"].data_ptr(),
-                            N, sp)
-        if ev is not None:
-            ev[3].record(stream)
+    def weight(s):
+        return lib.quant_weight_offline(s["w"], N, K, K, hb, s["wc"], s["ws"], s["wg"], sp)
+
+    def act(s):
+        return lib.rotate_quant_act(s["x"], M, K, K, hb, _lib.W4A4_ACT_SYM_TOKEN, s["xc"], s["xs"], None, sp)
+
+    def gemm(s):
+        return lib.w4a4_gemm(s["xc"], s["xs"], None, _lib.W4A4_ACT_SYM_TOKEN, s["wc"], s["ws"], None,
+                             M, N, K, s["y"], N, sp)
+
+    def check(st):
         if st:
             raise RuntimeError(f"W4A4 call failed: {_lib.last_error()}")
 
     for i in range(args.warmup):
-        step(sets[i % NSETS])
+        s = ptrs[i % NSETS]
+        check(weight(s) | act(s) | gemm(s))
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The GEMM launch of every timed step carries its own pair of events: the
+    # runtime stamps the kernel's start and end into them (no marker packets
+    # between kernels).  Arming every launch costs enough host time to make
+    # the step launch-bound, so the two rotate+quantize kernels are timed the
+    # same way in a second pass right after the timed region.
+    arm = lib.w4a4_time_next_launch
+    ev = [hev.pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % NSETS], evs[i])
+        s = ptrs[i % NSETS]
+        st = weight(s) | act(s)
+        arm(*ev[i])
+        st |= gemm(s)
+        check(st)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
     ms_step = (t1 - t0) * 1e3 / args.steps
-    kt = {"quant_weight_offline": 0.0, "rotate_quant_act": 0.0, "w4a4_gemm": 0.0}
-    for e in evs:
-        kt["quant_weight_offline"] += e[0].elapsed_time(e[1])
-        kt["rotate_quant_act"] += e[1].elapsed_time(e[2])
-        kt["w4a4_gemm"] += e[2].elapsed_time(e[3])
-    kt = {k: v / args.steps for k, v in kt.items()}      # ms per launch
+    kt = {"w4a4_gemm": sum(hev.elapsed(*e) for e in ev) / args.steps}
+
+    ev2 = [hev.pair() for _ in range(args.steps)]
+    for i in range(args.steps):
+        s = ptrs[i % NSETS]
+        arm(*ev[i])
+        st = weight(s)
+        arm(*ev2[i])
+        st |= act(s)
+        st |= gemm(s)
+        check(st)
+    torch.cuda.synchronize()
+    kt["quant_weight_offline"] = sum(hev.elapsed(*e) for e in ev) / args.steps
+    kt["rotate_quant_act"] = sum(hev.elapsed(*e) for e in ev2) / args.steps
+    hev.close()
+
     ops = 2.0 * M * N * K
     gemm_tops = ops / (kt["w4a4_gemm"] * 1e-3) / 1e12
     act_bytes = 2 * M * K + M * K // 2 + 4 * M
@@ -363,7 +392,7 @@ def main() -> int:
                    "M": M, "N": N, "K": K, "had_block": block},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic, "kernel": "w4a4_gemm (gemm_tile_kernel<sym>)",
+                     "traffic": traffic, "kernel": "w4a4_gemm (gemm_adirect_kernel, 256x128 tiles)",
                      "per_launch_ops": ops, "avg_launch_ms": round(kt["w4a4_gemm"], 5)},
         "kernels": {
             "w4a4_gemm": {"avg_ms": round(kt["w4a4_gemm"], 5), "TOPS": round(gemm_tops, 1),
@@ -375,7 +404,6 @@ def main() -> int:
                                      "GB/s": round(w_gbs, 1),
                                      "frac_hbm_peak": round(w_gbs / HBM_PEAK_GBS, 4), "bytes": w_bytes},
         },
-        "event_ms_per_step": round(sum(kt.values()), 5),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

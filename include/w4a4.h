@@ -19,7 +19,8 @@
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller; the
  *    library allocates no device memory and keeps no state besides its code
- *    objects and a per-device architecture check.
+ *    objects, a per-device architecture check and, per host thread, the
+ *    last error message and the events armed by w4a4_time_next_launch.
  *  - Every call is asynchronous and ordered on `stream` (a hipStream_t;
  *    NULL means the null stream).  Buffers must stay alive until the stream
  *    work completes.  Outputs must not alias inputs.
@@ -176,6 +177,17 @@ W4A4_API const char* w4a4_last_error(void);
 
 /* W4A4_ABI_VERSION of the loaded library. */
 W4A4_API int32_t w4a4_abi_version(void);
+
+/* Timing hook, outside the method: arms two HIP events (hipEvent_t values
+ * the caller created, e.g. with hipEventCreate, and still owns) for the next
+ * entry-point call on this host thread.  The kernel that call enqueues is
+ * launched with them attached, so the runtime writes the kernel's own start
+ * and end timestamps into them and hipEventElapsedTime(start, stop) is its
+ * device duration, without the queue gaps that hipEventRecord markers put
+ * between kernels.  The entry point disarms the pair when it returns, also
+ * when it fails or enqueues nothing.  Both NULL disarms; exactly one NULL is
+ * W4A4_ERR_NULL.  Per host thread; needs no device. */
+W4A4_API w4a4_status w4a4_time_next_launch(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,12 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local w4a4::LaunchTiming g_timing;
+
+// Disarms the timing events when an entry point returns, launched or not.
+struct TimingScope {
+  ~TimingScope() { g_timing = w4a4::LaunchTiming{}; }
+};
 
 w4a4_status fail(w4a4_status s, const char* fmt, ...) {
   char buf[512];
@@ -86,15 +92,32 @@ w4a4_status check_rows_k(int64_t rows, int64_t K, int64_t ld, const char* rn, co
 
 }  // namespace
 
+namespace w4a4 {
+void arm_launch_timing(hipEvent_t start, hipEvent_t stop) { g_timing = LaunchTiming{start, stop}; }
+LaunchTiming take_launch_timing() {
+  const LaunchTiming t = g_timing;
+  g_timing = LaunchTiming{};
+  return t;
+}
+}  // namespace w4a4
+
 extern "C" {
 
 const char* w4a4_last_error(void) { return g_err.c_str(); }
 
 int32_t w4a4_abi_version(void) { return W4A4_ABI_VERSION; }
 
+w4a4_status w4a4_time_next_launch(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(W4A4_ERR_NULL, "start_event and stop_event must both be NULL or both non-NULL");
+  w4a4::arm_launch_timing(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+  return ok();
+}
+
 w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
                              int32_t had_block, int32_t act_mode, uint8_t* codes, float* scales,
                              uint8_t* zeros, void* stream) {
+  TimingScope timing_scope;
   if (act_mode != W4A4_ACT_SYM_TOKEN && act_mode != W4A4_ACT_ASYM_G128)
     return fail(W4A4_ERR_MODE, "act_mode=%d is not W4A4_ACT_SYM_TOKEN or W4A4_ACT_ASYM_G128", act_mode);
   if (had_block != W4A4_HAD_FULL && had_block != W4A4_HAD_128)
@@ -134,6 +157,7 @@ w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_
 w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, int64_t ldw,
                                  int32_t had_block, uint8_t* codes, float* scales, int32_t* gsum,
                                  void* stream) {
+  TimingScope timing_scope;
   if (had_block != W4A4_HAD_FULL && had_block != W4A4_HAD_128)
     return fail(W4A4_ERR_MODE, "had_block=%d is not W4A4_HAD_FULL or W4A4_HAD_128", had_block);
   if (w4a4_status s = check_rows_k(N, K, ldw, "N", "ldw")) return s;
@@ -163,6 +187,7 @@ w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, const uint8
                       int32_t act_mode, const uint8_t* w_codes, const float* w_scales,
                       const int32_t* w_gsum, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,
                       void* stream) {
+  TimingScope timing_scope;
   (void)w_gsum;   // zero-points are removed before the product; group sums are not needed
   if (act_mode != W4A4_ACT_SYM_TOKEN && act_mode != W4A4_ACT_ASYM_G128)
     return fail(W4A4_ERR_MODE, "act_mode=%d is not W4A4_ACT_SYM_TOKEN or W4A4_ACT_ASYM_G128", act_mode);
@@ -202,6 +227,7 @@ w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, const uint8
 w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64_t S, int64_t D,
                              int64_t stride_b, int64_t stride_h, int64_t stride_s, uint8_t* codes,
                              float* scales, uint8_t* zeros, void* stream) {
+  TimingScope timing_scope;
   if (D != 128) return fail(W4A4_ERR_SHAPE, "D=%lld must be 128", (long long)D);
   if (B < 0 || H < 0 || S < 0) return fail(W4A4_ERR_SHAPE, "B, H and S must be >= 0");
   if (H >= (int64_t(1) << 31) || S >= (int64_t(1) << 31) ||

@@ -490,7 +490,7 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
   if (p.M == 0) return hipSuccess;
   if (mode == kModeSym && p.M <= 16) {
     const int64_t grid = (p.N + 15) / 16;
-    hipLaunchKernelGGL(gemm_decode_kernel, dim3((uint32_t)grid), dim3(256), 0, st, p);
+    W4A4_LAUNCH(gemm_decode_kernel, dim3((uint32_t)grid), dim3(256), 0, st, p);
     return hipGetLastError();
   }
   if (mode == kModeSym) {
@@ -501,19 +501,19 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     if (p.M > 512) {
       const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
       if (grid >= 512)
-        hipLaunchKernelGGL((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+        W4A4_LAUNCH((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_adirect_kernel<16, 1, 4>), dim3((uint32_t)grid), dim3(1024), 0, st, p);
+        W4A4_LAUNCH((gemm_adirect_kernel<16, 1, 4>), dim3((uint32_t)grid), dim3(1024), 0, st, p);
     } else {
       const int64_t grid = ((p.M + 63) / 64) * ((p.N + BN - 1) / BN);
-      hipLaunchKernelGGL((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
+      W4A4_LAUNCH((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
     }
     return hipGetLastError();
   }
   // asymmetric per-group activations: 128-row tiles of 8 waves (16 x 128 each);
   // the per-group fp32 fold needs the registers of a wider wave tile
   const int64_t grid = ((p.M + 127) / 128) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_adirect_asym_kernel<8, 1, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+  W4A4_LAUNCH((gemm_adirect_asym_kernel<8, 1, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Kernel parameter blocks and launchers (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,5 +51,23 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st);
 hipError_t gemm_prepare_device();   // once per device, before the first GEMM launch
+
+// Optional per-launch timing: events armed on this host thread are attached to
+// the next kernel launch (the runtime writes the kernel's own start and end
+// timestamps into them) and then disarmed.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+void arm_launch_timing(hipEvent_t start, hipEvent_t stop);
+LaunchTiming take_launch_timing();
+
+// Every kernel of the library is launched through this, so an armed pair of
+// timing events always lands on the kernel an entry point enqueues.
+#define W4A4_LAUNCH(KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                 \
+  do {                                                                                     \
+    const ::w4a4::LaunchTiming t_ = ::w4a4::take_launch_timing();                          \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, (uint32_t)(LDS), STREAM, t_.start, t_.stop, \
+                          0u, __VA_ARGS__);                                                \
+  } while (0)
 
 }  // namespace w4a4

@@ -297,8 +297,8 @@ namespace {
 
 template <int MODE, int LOGF, bool GSUM, bool STRIDED>
 hipError_t launch_t(const RQParams& p, int threads, size_t lds, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED>), dim3((uint32_t)grid),
-                     dim3(threads), lds, st, p);
+  W4A4_LAUNCH((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED>), dim3((uint32_t)grid),
+              dim3(threads), lds, st, p);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-              "w4a4_last_error", "w4a4_abi_version"):
+              "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch"):
         assert n in names
 
 
@@ -120,6 +120,18 @@ def test_gemm_validation(args, status):
 ])
 def test_kv_validation(args, status):
     assert _lib.call("kv_rotate_quant4", *args) == status
+
+
+def test_time_next_launch_arming():
+    """The timing hook needs no device: both NULL or both set; an entry point
+    that fails validation disarms it (the next launch is not timed by stale events)."""
+    assert _lib.call("w4a4_time_next_launch", A, NUL) == _lib.W4A4_ERR_NULL
+    assert _lib.call("w4a4_time_next_launch", NUL, A) == _lib.W4A4_ERR_NULL
+    assert _lib.call("w4a4_time_next_launch", NUL, NUL) == _lib.W4A4_OK
+    assert _lib.call("w4a4_time_next_launch", A, A + 16) == _lib.W4A4_OK
+    # a failing call consumes the armed pair; nothing reads the (host) pointers
+    assert _lib.call("rotate_quant_act", A, 4, 100, 128, 128, 0, A, A, NUL, NUL) == _lib.W4A4_ERR_SHAPE
+    assert _lib.call("w4a4_time_next_launch", NUL, NUL) == _lib.W4A4_OK
 
 
 def test_no_device_is_a_device_error():
