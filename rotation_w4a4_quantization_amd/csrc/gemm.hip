@@ -26,6 +26,24 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 namespace {
 
+// Tile coordinates of this workgroup.  Tiles are walked in groups of 16 tile
+// rows, column by column inside a group, so the workgroups resident at one
+// time cover a 16-row block of tiles and share both its A rows and its B
+// rows in L2 (row-major order would stream every B tile once per pair of
+// tile rows); measured 2-5% faster on the q_proj, down_proj and gate/up
+// shapes.  The mapping is a bijection of [0, tiles_m * tiles_n).
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  constexpr int64_t GM = 16;
+  const int64_t pid = blockIdx.x;
+  const int64_t in_group = GM * tiles_n;
+  const int64_t gid = pid / in_group;
+  const int64_t first_m = gid * GM;
+  const int64_t gsz = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+  const int64_t r = pid - gid * in_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
+}
+
 constexpr int BN = 128, BK = 128;   // BK in 4-bit elements
 constexpr int LROW = 128;                      // LDS bytes per int8 row (one K step)
 
@@ -108,7 +126,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BMD, n0 = tn * BN;
   const int nkt = p.K / BK;
   const int64_t ldc = p.K / 2;
@@ -265,7 +285,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BMD, n0 = tn * BN;
   const int nkt = p.K / BK;
   const int G = nkt;
