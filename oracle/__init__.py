@@ -6,4 +6,4 @@ code with the HIP library; the two meet only through the seeded inputs in
 `workloads`.
 """
 from .w4a4 import *  # noqa: F401,F403
-from .w4a4 import hadamard, rotate, rotate_normalized  # noqa: F401
+from .w4a4 import apply_signs, hadamard, rotate, rotate_normalized  # noqa: F401

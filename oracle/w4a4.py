@@ -16,7 +16,9 @@ Pages cited (titles; the section follows the dash):
 
 Readings taken where the pages leave a step open (each is repeated in the
 function that uses it):
-  * Hadamard = Sylvester construction in natural order, no random signs.
+  * Hadamard = Sylvester construction in natural order.  The randomized
+    Hadamard of [QR] "Activation scheme" is diag(d) H with a +-1 vector d
+    that the caller draws and passes in (`signs`); None means d = 1.
   * Rotation acts on every row along K, in contiguous aligned blocks of b
     (b = 128 or b = K), i.e. Q = I (x) H_b / sqrt(b).
   * Symmetric INT4: 15 levels -7..7, scale = max|y| / 7, no clipping.
@@ -56,8 +58,26 @@ def hadamard(n: int) -> np.ndarray:
     return h
 
 
-def rotate(x, block: int) -> np.ndarray:
-    """Unnormalized block rotation z = x . (I (x) H_block) of every row, float64.
+def apply_signs(x, signs) -> np.ndarray:
+    """x . diag(d) in float64: column k of every row times d[k] (+-1).
+
+    [QR] "Activation scheme": QuaRot's rotations are randomized Hadamard
+    matrices; [ROT] "The recipe": "random-hadamard" vs the fixed "hadamard".
+    Read as Q = diag(d) H / sqrt(b) with d a +-1 vector over all K columns,
+    the same for activations and weights (Q stays orthogonal since d*d = 1).
+    signs None: no flip.
+    """
+    x = np.asarray(x, dtype=F64)
+    if signs is None:
+        return x
+    d = np.asarray(signs, dtype=F64).reshape(-1)
+    if d.shape[0] != x.shape[-1] or not np.all(np.abs(d) == 1.0):
+        raise ValueError("signs must be a +-1 vector with one entry per column")
+    return x * d[None, :]
+
+
+def rotate(x, block: int, signs=None) -> np.ndarray:
+    """Unnormalized block rotation z = x . diag(d) . (I (x) H_block) of every row, float64.
 
     [ROT] "A rotation changes nothing": Y = X W^T = (XQ)(WQ)^T for orthogonal Q.
     [ROT] "Gotchas" (block size): a 128-wide block mixes channels in groups of
@@ -67,7 +87,7 @@ def rotate(x, block: int) -> np.ndarray:
     For fp16 inputs every partial sum is a multiple of 2^-24 below 2^29, so
     the float64 product is exact whatever order BLAS sums in.
     """
-    x = np.asarray(x, dtype=F64)
+    x = apply_signs(x, signs)
     R, K = x.shape
     if K % block:
         raise ValueError("K must be a multiple of the Hadamard block")
@@ -76,9 +96,9 @@ def rotate(x, block: int) -> np.ndarray:
     return z.reshape(R, K)
 
 
-def rotate_normalized(x, block: int) -> np.ndarray:
-    """y = x . Q with Q = I (x) H_block / sqrt(block)  ([ROT] "A rotation changes nothing")."""
-    return rotate(x, block) / np.sqrt(block)
+def rotate_normalized(x, block: int, signs=None) -> np.ndarray:
+    """y = x . Q with Q = diag(d) (I (x) H_block) / sqrt(block)  ([ROT] "A rotation changes nothing")."""
+    return rotate(x, block, signs) / np.sqrt(block)
 
 
 # --------------------------------------------------------------------------
@@ -270,15 +290,16 @@ def int_gemm_groups(u, zp, qw, group: int = 128) -> np.ndarray:
 # --------------------------------------------------------------------------
 # End-to-end pieces of the path
 # --------------------------------------------------------------------------
-def rotate_quant_act(x, block: int, mode: str) -> dict:
+def rotate_quant_act(x, block: int, mode: str, signs=None) -> dict:
     """Online activation step: rotate each token, quantize, pack.
 
     [ROT] "Where the rotations go": rotations that cannot be folded into the
     weights cost one fast Hadamard transform per token, fused with the
     quantization of the activations.  mode "sym": one scale per token;
-    mode "asym": asymmetric per group of 128 with a zero-point.
+    mode "asym": asymmetric per group of 128 with a zero-point.  signs: the
+    randomized-Hadamard diagonal (see `apply_signs`), or None.
     """
-    z = rotate(x, block)
+    z = rotate(x, block, signs)
     if mode == "sym":
         d = quant_sym_rows(z, block)
         d["packed"] = pack_nibbles(d["codes"])
@@ -291,14 +312,15 @@ def rotate_quant_act(x, block: int, mode: str) -> dict:
     return d
 
 
-def quant_weight_offline(w, block: int) -> dict:
+def quant_weight_offline(w, block: int, signs=None) -> dict:
     """Offline weight step: rotate each output channel's row, symmetric INT4
     per output channel, pack, and the per-128 group sums of the codes.
 
     [ROT] "Where the rotations go": rotations applied to weights are folded
-    offline and cost nothing at run time.
+    offline and cost nothing at run time.  signs: the same diagonal the
+    activations use, or None.
     """
-    z = rotate(w, block)
+    z = rotate(w, block, signs)
     d = quant_sym_rows(z, block)
     d["packed"] = pack_nibbles(d["codes"])
     d["gsum"] = group_sums(d["codes"], 128)
@@ -306,14 +328,14 @@ def quant_weight_offline(w, block: int) -> dict:
     return d
 
 
-def w4a4_linear(x, w, block: int, mode: str = "sym") -> dict:
+def w4a4_linear(x, w, block: int, mode: str = "sym", signs=None) -> dict:
     """Y_hat = Q(XQ) . Q(WQ)^T and the float64 X W^T it approximates.
 
     [ROT] "A rotation changes nothing" (invariance) and "What it buys in 4
     bits" (the quantized product).
     """
-    a = rotate_quant_act(x, block, mode)
-    wq = quant_weight_offline(w, block)
+    a = rotate_quant_act(x, block, mode, signs)
+    wq = quant_weight_offline(w, block, signs)
     if mode == "sym":
         acc = int_gemm(a["codes"], wq["codes"])
         y = epilogue_sym_f64(acc, a["scale"], wq["scale"])
@@ -323,7 +345,7 @@ def w4a4_linear(x, w, block: int, mode: str = "sym") -> dict:
     return dict(act=a, wq=wq, acc=acc, y=y)
 
 
-def kv_rotate_quant(kv, block: int = 128) -> dict:
+def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
     """KV cache step: rotate every (batch, head, token) vector of head_dim 128
     with one 128-point Hadamard, then asymmetric INT4 with a zero-point, one
     group per vector.
@@ -335,7 +357,7 @@ def kv_rotate_quant(kv, block: int = 128) -> dict:
     shape = kv.shape
     D = shape[-1]
     flat = kv.reshape(-1, D)
-    z = rotate(flat, block)
+    z = rotate(flat, block, signs)
     d = quant_asym_groups(z, block, D)
     d["packed"] = pack_nibbles(d["codes"]).reshape(*shape[:-1], D // 2)
     d["scale"] = d["scale"].reshape(shape[:-1])

@@ -407,3 +407,70 @@ def test_kv_oracle_shapes_and_dequant():
     y = O.rotate_normalized(d["KV"].reshape(-1, 128), 128)
     yh = O.dequant_asym_groups(r["codes"], r["scale"].reshape(-1, 1), r["zp"].reshape(-1, 1))
     assert np.all(np.abs(y - yh) <= 0.5 * r["scale"].reshape(-1, 1) * (1 + 1e-5))
+
+
+# ---------------------------------------------------------------- randomized Hadamard (diag(d) H)
+def test_signed_rotation_worked_example():
+    """Hand-computed: d = (1, -1, 1, 1), x = (1, 2, 3, 4): d*x = (1, -2, 3, 4) and
+    H4 (d*x) = (1-2+3+4, 1+2+3-4, 1-2-3-4, 1+2-3+4) = (6, 2, -8, 4)."""
+    z = O.rotate(np.array([[1.0, 2.0, 3.0, 4.0]]), 4, signs=np.array([1.0, -1.0, 1.0, 1.0]))
+    assert z.tolist() == [[6.0, 2.0, -8.0, 4.0]]
+
+
+def test_all_plus_signs_is_the_plain_rotation():
+    x = WL.small_random(11, 5, 512)
+    for block in (128, 512):
+        assert np.array_equal(O.rotate(x, block, signs=np.ones(512)), O.rotate(x, block))
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 256])
+def test_signed_hadamard_orthogonal(n):
+    """(diag(d) H)^T (diag(d) H) = H^T diag(d)^2 H = n I, exactly in integers."""
+    d = WL.hadamard_signs(n, seed=n).astype(np.int64)
+    m = d[:, None] * O.hadamard(n)
+    assert np.array_equal(m.T @ m, n * np.eye(n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("block", [128, 1024])
+def test_signed_invariance_and_mismatch(block):
+    """Same d on both sides: X W^T is unchanged to float64 rounding; different d
+    on the two sides: the product is destroyed (the diagonal must be shared)."""
+    x = WL.small_random(21, 64, 1024, outlier_cols=(5,), mult=30.0).astype(np.float64)
+    w = WL.small_random(22, 48, 1024, std=0.02).astype(np.float64)
+    d = WL.hadamard_signs(1024, seed=3)
+    ref = x @ w.T
+    same = O.rotate_normalized(x, block, d) @ O.rotate_normalized(w, block, d).T
+    assert np.linalg.norm(same - ref) / np.linalg.norm(ref) < 1e-10
+    other = O.rotate_normalized(x, block, d) @ O.rotate_normalized(w, block, WL.hadamard_signs(1024, seed=4)).T
+    assert np.linalg.norm(other - ref) / np.linalg.norm(ref) > 0.5
+
+
+@pytest.mark.parametrize("n,j", [(128, 5), (128, 77), (512, 300)])
+def test_signed_outlier_codes_closed_form(n, j):
+    """x = M e_j: d*x = M d_j e_j, so z = M d_j h_j and the symmetric codes are
+    7 d_j (-1)^popcount(i & j) with scale M / (7 sqrt(n)) -- exactly."""
+    m = 96.0
+    x = np.zeros((1, n))
+    x[0, j] = m
+    d = WL.hadamard_signs(n, seed=j)
+    q = O.rotate_quant_act(x, n, "sym", signs=d)
+    expect = np.array([7 * int(d[j]) * (-1) ** bin(i & j).count("1") for i in range(n)])
+    assert np.array_equal(q["codes"][0], expect)
+    assert q["scale"][0] == np.float32(np.float32(m) / np.float32(7.0 * math.sqrt(n)))
+
+
+def test_signed_rotation_lowers_int4_product_error():
+    """The randomized rotation keeps the page's effect: the INT4 product error
+    with diag(d) H is far below the unrotated one (q_proj-like outliers)."""
+    d = WL.qproj(M=256, with_w=False)
+    x = d["X"].astype(np.float64)
+    w = WL.qproj_weight()[:256].astype(np.float64)
+    s = WL.hadamard_signs(4096, seed=1)
+    plain_q = O.quant_sym_rows(x, 1)
+    plain_w = O.quant_sym_rows(w, 1)
+    e_plain = O.product_error(x, w, O.dequant_sym_rows(plain_q["codes"], plain_q["scale"]),
+                              O.dequant_sym_rows(plain_w["codes"], plain_w["scale"]))
+    lin = O.w4a4_linear(x, w, 128, "sym", signs=s)
+    ref = x @ w.T
+    e_rot = np.linalg.norm(lin["y"] - ref) / np.linalg.norm(ref)
+    assert e_rot < 0.5 * e_plain

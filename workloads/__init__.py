@@ -154,3 +154,11 @@ def small_random(seed: int, rows: int, cols: int, std: float = 1.0,
     rng = np.random.default_rng(np.random.SeedSequence(55_000 + seed))
     return _normal_fp16(rng, rows, cols, std, scale_cols=np.asarray(outlier_cols, dtype=np.int64),
                         mult=mult)
+
+
+def hadamard_signs(n: int, seed: int = 0) -> np.ndarray:
+    """n fp16 values, each +1.0 or -1.0 with probability 1/2: the random
+    diagonal of a randomized Hadamard rotation.  The draw only; what the
+    signs do is the method's business, not this module's."""
+    rng = np.random.default_rng(np.random.SeedSequence(66_000 + seed))
+    return np.where(rng.integers(0, 2, size=n) == 0, 1.0, -1.0).astype(np.float16)
