@@ -314,10 +314,11 @@ def main() -> int:
     ptrs = [{k: v.data_ptr() for k, v in s.items()} for s in sets]
 
     def weight(s):
-        return lib.quant_weight_offline(s["w"], N, K, K, hb, s["wc"], s["ws"], s["wg"], sp)
+        return lib.quant_weight_offline(s["w"], N, K, K, hb, None, s["wc"], s["ws"], s["wg"], sp)
 
     def act(s):
-        return lib.rotate_quant_act(s["x"], M, K, K, hb, _lib.W4A4_ACT_SYM_TOKEN, s["xc"], s["xs"], None, sp)
+        return lib.rotate_quant_act(s["x"], M, K, K, hb, None, _lib.W4A4_ACT_SYM_TOKEN, s["xc"], s["xs"], None,
+                                    sp)
 
     def gemm(s):
         return lib.w4a4_gemm(s["xc"], s["xs"], None, _lib.W4A4_ACT_SYM_TOKEN, s["wc"], s["ws"], None,

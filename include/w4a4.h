@@ -84,7 +84,22 @@ typedef enum {
 enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
 enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
 
-#define W4A4_ABI_VERSION 1
+#define W4A4_ABI_VERSION 2
+
+/*
+ * had_signs (the three rotate calls): NULL, or a device array of K fp16
+ * values (D = 128 for kv_rotate_quant4), each +1.0 or -1.0, 16-byte aligned.
+ * Non-NULL turns the rotation into the randomized Hadamard Q = diag(d) H / sqrt(b):
+ * element k of every row is multiplied by d[k] (its sign bit is flipped
+ * when d[k] carries one) before the per-block transform.  X and W must use
+ * the same d (Q stays orthogonal, so X W^T is unchanged); the codes do not
+ * record it.  Only the sign bit of each entry is read.
+ *   Page "QuaRot (rotation-based outlier removal, W4A4KV4)", field
+ *   "Activation scheme" (randomized Hadamard rotations); page "Rotations for
+ *   4-Bit Activations: QuaRot, SpinQuant, and Friends", sections "Where the
+ *   rotations go" and "The recipe" (random vs fixed Hadamard).  The random
+ *   signs are drawn by the caller and passed in.
+ */
 
 /*
  * rotate_quant_act - online activation step: per row of X, one fast
@@ -106,7 +121,7 @@ enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
  *   codes   [M][K/2] packed nibbles (written).
  */
 W4A4_API w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
-                             int32_t had_block, int32_t act_mode,
+                             int32_t had_block, const uint16_t* had_signs, int32_t act_mode,
                              uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
 
 /*
@@ -123,7 +138,7 @@ W4A4_API w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t 
  *   gsum    NULL, or [N][K/128] int32: sum of the 128 codes of each group.
  */
 W4A4_API w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, int64_t ldw,
-                                 int32_t had_block,
+                                 int32_t had_block, const uint16_t* had_signs,
                                  uint8_t* codes, float* scales, int32_t* gsum, void* stream);
 
 /*
@@ -170,6 +185,7 @@ W4A4_API w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, co
  */
 W4A4_API w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64_t S, int64_t D,
                              int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                             const uint16_t* had_signs,
                              uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
 
 /* Message of the last failed call on this thread ("" after a success). */

@@ -7,6 +7,9 @@ exception.  Every step of the computation runs in the library's kernels.
 
     codes, scales, zeros = rotate_quant_act(x, had_block=128, act_mode="sym")
     wq, ws, gsum = quant_weight_offline(w, had_block=128)
+    # randomized Hadamard: the same fp16 +-1 vector d (length K) on both sides
+    codes, scales, zeros = rotate_quant_act(x, had_block=128, signs=d)
+    wq, ws, gsum = quant_weight_offline(w, had_block=128, signs=d)
     y = w4a4_gemm(codes, scales, zeros, wq, ws, act_mode="sym")
     kc, ks, kz = kv_rotate_quant4(kv)
 """
@@ -52,12 +55,26 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _signs(signs, n: int, dev):
+    """Check an optional randomized-Hadamard sign vector: fp16 [n], contiguous, on dev."""
+    if signs is None:
+        return None
+    _need(signs, torch.float16, "signs")
+    if signs.dim() != 1 or signs.shape[0] != n or not signs.is_contiguous():
+        raise ValueError(f"signs must be a contiguous fp16 vector of length {n}")
+    if signs.device != dev:
+        raise ValueError("signs must be on the same device as the data")
+    return signs
+
+
 def abi_version() -> int:
     return int(_lib.load().w4a4_abi_version())
 
 
-def rotate_quant_act(x: torch.Tensor, had_block: int = 128, act_mode: str = "sym"):
+def rotate_quant_act(x: torch.Tensor, had_block: int = 128, act_mode: str = "sym", signs=None):
     """Rotate every row of fp16 X [M, K] and quantize it to packed INT4.
+
+    signs: None, or fp16 [K] of +-1 (randomized Hadamard, diag(signs) H).
 
     Returns (codes uint8 [M, K/2], scales fp32 [M] or [M, K/128],
     zeros uint8 [M, K/128] or None).
@@ -76,14 +93,17 @@ def rotate_quant_act(x: torch.Tensor, had_block: int = 128, act_mode: str = "sym
         scales = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
         zeros = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
     hb = W4A4_HAD_128 if had_block == 128 else (W4A4_HAD_FULL if had_block in (0, K, "full") else -1)
-    st = _lib.call("rotate_quant_act", _ptr(x), M, K, x.stride(0), hb, mode, _ptr(codes),
+    sg = _signs(signs, K, dev)
+    st = _lib.call("rotate_quant_act", _ptr(x), M, K, x.stride(0), hb, _ptr(sg), mode, _ptr(codes),
                    _ptr(scales), _ptr(zeros), _stream(dev))
     _check(st, "rotate_quant_act")
     return codes, scales, zeros
 
 
-def quant_weight_offline(w: torch.Tensor, had_block: int = 128, with_gsum: bool = True):
+def quant_weight_offline(w: torch.Tensor, had_block: int = 128, with_gsum: bool = True, signs=None):
     """Rotate and quantize fp16 W [N, K] per output channel.
+
+    signs: None, or the same fp16 [K] +-1 vector the activations use.
 
     Returns (codes uint8 [N, K/2], scales fp32 [N], gsum int32 [N, K/128] or None).
     """
@@ -96,7 +116,8 @@ def quant_weight_offline(w: torch.Tensor, had_block: int = 128, with_gsum: bool 
     scales = torch.empty((N,), dtype=torch.float32, device=dev)
     gsum = torch.empty((N, K // 128), dtype=torch.int32, device=dev) if with_gsum else None
     hb = W4A4_HAD_128 if had_block == 128 else (W4A4_HAD_FULL if had_block in (0, K, "full") else -1)
-    st = _lib.call("quant_weight_offline", _ptr(w), N, K, w.stride(0), hb, _ptr(codes),
+    sg = _signs(signs, K, dev)
+    st = _lib.call("quant_weight_offline", _ptr(w), N, K, w.stride(0), hb, _ptr(sg), _ptr(codes),
                    _ptr(scales), _ptr(gsum), _stream(dev))
     _check(st, "quant_weight_offline")
     return codes, scales, gsum
@@ -131,8 +152,10 @@ def w4a4_gemm(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum=None, act_mo
     return y
 
 
-def kv_rotate_quant4(kv: torch.Tensor):
+def kv_rotate_quant4(kv: torch.Tensor, signs=None):
     """Rotate + asymmetric INT4 of a KV cache [B, H, S, 128] fp16 (last dim contiguous).
+
+    signs: None, or fp16 [128] of +-1 (randomized Hadamard over the head dim).
 
     Returns (codes uint8 [B, H, S, 64], scales fp32 [B, H, S], zeros uint8 [B, H, S]).
     """
@@ -145,7 +168,8 @@ def kv_rotate_quant4(kv: torch.Tensor):
     scales = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     zeros = torch.empty((B, H, S), dtype=torch.uint8, device=dev)
     sb, sh, ss, _ = kv.stride()
-    st = _lib.call("kv_rotate_quant4", _ptr(kv), B, H, S, D, sb, sh, ss, _ptr(codes), _ptr(scales),
+    sg = _signs(signs, D, dev)
+    st = _lib.call("kv_rotate_quant4", _ptr(kv), B, H, S, D, sb, sh, ss, _ptr(sg), _ptr(codes), _ptr(scales),
                    _ptr(zeros), _stream(dev))
     _check(st, "kv_rotate_quant4")
     return codes, scales, zeros

@@ -21,10 +21,10 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 
 SIGNATURES = {
-    "rotate_quant_act": [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp],
-    "quant_weight_offline": [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
+    "rotate_quant_act": [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp],
+    "quant_weight_offline": [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "w4a4_gemm": [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
-    "kv_rotate_quant4": [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "kv_rotate_quant4": [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "w4a4_time_next_launch": [_vp, _vp],
 }
 

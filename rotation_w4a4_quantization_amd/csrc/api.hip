@@ -115,8 +115,8 @@ w4a4_status w4a4_time_next_launch(void* start_event, void* stop_event) {
 }
 
 w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
-                             int32_t had_block, int32_t act_mode, uint8_t* codes, float* scales,
-                             uint8_t* zeros, void* stream) {
+                             int32_t had_block, const uint16_t* had_signs, int32_t act_mode,
+                             uint8_t* codes, float* scales, uint8_t* zeros, void* stream) {
   TimingScope timing_scope;
   if (act_mode != W4A4_ACT_SYM_TOKEN && act_mode != W4A4_ACT_ASYM_G128)
     return fail(W4A4_ERR_MODE, "act_mode=%d is not W4A4_ACT_SYM_TOKEN or W4A4_ACT_ASYM_G128", act_mode);
@@ -133,12 +133,14 @@ w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_
     return fail(W4A4_ERR_MODE, "zeros must be NULL in symmetric mode");
   if (act_mode == W4A4_ACT_ASYM_G128 && !zeros)
     return fail(W4A4_ERR_MODE, "zeros must be non-NULL in asymmetric mode");
-  if (!aligned16(x_f16) || !aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)))
+  if (!aligned16(x_f16) || !aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)) ||
+      (had_signs && !aligned16(had_signs)))
     return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
   if (w4a4_status s = check_device()) return s;
 
   w4a4::RQParams p{};
   p.x = x_f16;
+  p.signs = had_signs;
   p.codes = codes;
   p.scales = scales;
   p.zeros = zeros;
@@ -155,8 +157,8 @@ w4a4_status rotate_quant_act(const uint16_t* x_f16, int64_t M, int64_t K, int64_
 }
 
 w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, int64_t ldw,
-                                 int32_t had_block, uint8_t* codes, float* scales, int32_t* gsum,
-                                 void* stream) {
+                                 int32_t had_block, const uint16_t* had_signs, uint8_t* codes,
+                                 float* scales, int32_t* gsum, void* stream) {
   TimingScope timing_scope;
   if (had_block != W4A4_HAD_FULL && had_block != W4A4_HAD_128)
     return fail(W4A4_ERR_MODE, "had_block=%d is not W4A4_HAD_FULL or W4A4_HAD_128", had_block);
@@ -165,12 +167,14 @@ w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, in
     return fail(W4A4_ERR_SHAPE, "full-width Hadamard needs K a power of two, got K=%lld", (long long)K);
   if (N == 0) return ok();   // nothing is read or written: pointers may be NULL
   if (!w_f16 || !codes || !scales) return fail(W4A4_ERR_NULL, "w_f16, codes and scales must be non-NULL");
-  if (!aligned16(w_f16) || !aligned16(codes) || !aligned16(scales) || (gsum && !aligned16(gsum)))
+  if (!aligned16(w_f16) || !aligned16(codes) || !aligned16(scales) || (gsum && !aligned16(gsum)) ||
+      (had_signs && !aligned16(had_signs)))
     return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
   if (w4a4_status s = check_device()) return s;
 
   w4a4::RQParams p{};
   p.x = w_f16;
+  p.signs = had_signs;
   p.codes = codes;
   p.scales = scales;
   p.gsum = gsum;
@@ -225,8 +229,9 @@ w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, const uint8
 }
 
 w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64_t S, int64_t D,
-                             int64_t stride_b, int64_t stride_h, int64_t stride_s, uint8_t* codes,
-                             float* scales, uint8_t* zeros, void* stream) {
+                             int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                             const uint16_t* had_signs, uint8_t* codes, float* scales,
+                             uint8_t* zeros, void* stream) {
   TimingScope timing_scope;
   if (D != 128) return fail(W4A4_ERR_SHAPE, "D=%lld must be 128", (long long)D);
   if (B < 0 || H < 0 || S < 0) return fail(W4A4_ERR_SHAPE, "B, H and S must be >= 0");
@@ -240,12 +245,14 @@ w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64
   if (rows == 0) return ok();   // nothing is read or written: pointers may be NULL
   if (!kv_f16 || !codes || !scales || !zeros)
     return fail(W4A4_ERR_NULL, "kv_f16, codes, scales and zeros must be non-NULL");
-  if (!aligned16(kv_f16) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros))
+  if (!aligned16(kv_f16) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros) ||
+      (had_signs && !aligned16(had_signs)))
     return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
   if (w4a4_status s = check_device()) return s;
 
   w4a4::RQParams p{};
   p.x = kv_f16;
+  p.signs = had_signs;
   p.codes = codes;
   p.scales = scales;
   p.zeros = zeros;

@@ -12,6 +12,7 @@ enum { kModeSym = 0, kModeAsym = 1 };
 // Rotate + quantize: one row of K fp16 values -> K/2 code bytes.
 struct RQParams {
   const uint16_t* x;
+  const uint16_t* signs;   // optional [K] fp16 +-1: the diagonal D of Q = D H / sqrt(b)
   uint8_t* codes;    // [rows][K/2]
   float* scales;     // sym: [rows]; asym: [rows][K/128]
   uint8_t* zeros;    // asym: [rows][K/128]

@@ -128,6 +128,22 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
   const uint32_t lane_off = lane_ok ? (uint32_t)(((int64_t)slot * p.ss + blk * 128 + q * 8) * 2) : 0x7FFFFFF0u;
   const int64_t ngroups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
 
+  // randomized Hadamard: the diagonal D depends on the column only, so each
+  // lane loads the sign bits of its 32 columns once and flips its inputs'
+  // signs (one XOR per pair of fp16 values) before the transform
+  const bool has_signs = p.signs != nullptr;
+  uint4 sg[4] = {};
+  if (has_signs) {
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.signs, (short)0, p.K * 2, 0x00020000);
+    const uint32_t soff = lane_ok ? (uint32_t)((blk * 128 + q * 8) * 2) : 0x7FFFFFF0u;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint4 d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, (int)soff, 64 * r4, 0));
+      sg[r4] = make_uint4(d.x & 0x80008000u, d.y & 0x80008000u, d.z & 0x80008000u, d.w & 0x80008000u);
+    }
+  }
+
   for (int64_t rgi = blockIdx.x; rgi < ngroups; rgi += gridDim.x) {
     const int64_t row0 = rgi * p.rows_per_wg;
     const int64_t row = row0 + slot;
@@ -150,6 +166,16 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         w[r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_off, 64 * r4, 0));
+    }
+
+    if (has_signs) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        w[r4].x ^= sg[r4].x;
+        w[r4].y ^= sg[r4].y;
+        w[r4].z ^= sg[r4].z;
+        w[r4].w ^= sg[r4].w;
+      }
     }
 
     // the first butterfly (element bit 0: the two halves of a dword) is fused

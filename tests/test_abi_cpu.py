@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for n in _declared():
         assert hasattr(lib, n), n
-    assert lib.w4a4_abi_version() == 1
+    assert lib.w4a4_abi_version() == 2
     src = open(HEADER).read()
     assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
 
@@ -55,25 +55,26 @@ NUL = None
 
 
 @pytest.mark.parametrize("args,status", [
-    ((NUL, 4, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 4, 128, 128, 128, 0, NUL, A, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 4, 128, 128, 128, 0, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 4, 100, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # K % 128
-    ((A, 4, 0, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
-    ((A, 4, 32768, 32768, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # K > 16384
-    ((A, -1, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
-    ((A, 4, 256, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # ldx < K
-    ((A, 4, 384, 384, 0, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),         # full needs 2^p
-    ((A, 4, 128, 132, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),       # ldx % 8
-    ((A + 2, 4, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),
-    ((A, 4, 128, 128, 64, 0, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),         # had_block
-    ((A, 4, 128, 128, 128, 2, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # act_mode
-    ((A, 4, 128, 128, 128, 0, A, A, A, NUL), _lib.W4A4_ERR_MODE),          # zeros in sym
-    ((A, 4, 128, 128, 128, 1, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # no zeros in asym
-    ((A, 4, 256, 256, 0, 1, A, A, A, NUL), _lib.W4A4_ERR_MODE),            # asym + full
-    ((A, 0, 128, 128, 128, 0, A, A, NUL, NUL), _lib.W4A4_OK),              # M == 0: no-op
-    ((NUL, 0, 128, 128, 128, 0, NUL, NUL, NUL, NUL), _lib.W4A4_OK),        # M == 0, NULL buffers
-    ((NUL, 0, 100, 128, 128, 0, NUL, NUL, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # sizes still checked
+    ((NUL, 4, 128, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, NUL, 0, NUL, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, NUL, 0, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 100, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # K % 128
+    ((A, 4, 0, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 32768, 32768, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # K > 16384
+    ((A, -1, 128, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 256, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),       # ldx < K
+    ((A, 4, 384, 384, 0, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),         # full needs 2^p
+    ((A, 4, 128, 132, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),       # ldx % 8
+    ((A + 2, 4, 128, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 4, 128, 128, 64, NUL, 0, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),         # had_block
+    ((A, 4, 128, 128, 128, NUL, 2, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # act_mode
+    ((A, 4, 128, 128, 128, NUL, 0, A, A, A, NUL), _lib.W4A4_ERR_MODE),          # zeros in sym
+    ((A, 4, 128, 128, 128, NUL, 1, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),        # no zeros in asym
+    ((A, 4, 256, 256, 0, NUL, 1, A, A, A, NUL), _lib.W4A4_ERR_MODE),            # asym + full
+    ((A, 0, 128, 128, 128, NUL, 0, A, A, NUL, NUL), _lib.W4A4_OK),              # M == 0: no-op
+    ((NUL, 0, 128, 128, 128, NUL, 0, NUL, NUL, NUL, NUL), _lib.W4A4_OK),        # M == 0, NULL buffers
+    ((NUL, 0, 100, 128, 128, NUL, 0, NUL, NUL, NUL, NUL), _lib.W4A4_ERR_SHAPE),  # sizes still checked
+    ((A, 4, 128, 128, 128, A + 2, 0, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),  # signs alignment
 ])
 def test_rotate_quant_act_validation(args, status):
     assert _lib.call("rotate_quant_act", *args) == status
@@ -81,12 +82,13 @@ def test_rotate_quant_act_validation(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((NUL, 4, 128, 128, 128, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 4, 128, 128, 128, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 4, 200, 200, 128, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
-    ((A, 4, 128, 128, 7, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),
-    ((A, 4, 128, 128, 128, A, A, A + 4, NUL), _lib.W4A4_ERR_ALIGN),
-    ((A, 0, 128, 128, 128, A, A, A, NUL), _lib.W4A4_OK),
+    ((NUL, 4, 128, 128, 128, NUL, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, NUL, A, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 200, 200, 128, NUL, A, A, NUL, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 128, 128, 7, NUL, A, A, NUL, NUL), _lib.W4A4_ERR_MODE),
+    ((A, 4, 128, 128, 128, NUL, A, A, A + 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 0, 128, 128, 128, NUL, A, A, A, NUL), _lib.W4A4_OK),
+    ((A, 4, 128, 128, 128, A + 8, A, A, NUL, NUL), _lib.W4A4_ERR_ALIGN),      # signs alignment
 ])
 def test_quant_weight_offline_validation(args, status):
     assert _lib.call("quant_weight_offline", *args) == status
@@ -110,13 +112,14 @@ def test_gemm_validation(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((NUL, 1, 1, 1, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 1, 1, 1, 128, 128, 128, 128, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
-    ((A, 1, 1, 1, 64, 64, 64, 64, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),      # D != 128
-    ((A, -1, 1, 1, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
-    ((A, 1, 1, 1, 128, 128, 128, 124, A, A, A, NUL), _lib.W4A4_ERR_ALIGN),
-    ((A, 1 << 16, 1 << 10, 1 << 6, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
-    ((A, 0, 4, 4, 128, 128, 128, 128, A, A, A, NUL), _lib.W4A4_OK),
+    ((NUL, 1, 1, 1, 128, 128, 128, 128, NUL, A, A, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 1, 1, 1, 128, 128, 128, 128, NUL, A, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 1, 1, 1, 64, 64, 64, 64, NUL, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),      # D != 128
+    ((A, -1, 1, 1, 128, 128, 128, 128, NUL, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 1, 1, 1, 128, 128, 128, 124, NUL, A, A, A, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 1 << 16, 1 << 10, 1 << 6, 128, 128, 128, 128, NUL, A, A, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 0, 4, 4, 128, 128, 128, 128, NUL, A, A, A, NUL), _lib.W4A4_OK),
+    ((A, 1, 1, 1, 128, 128, 128, 128, A + 4, A, A, A, NUL), _lib.W4A4_ERR_ALIGN),  # signs alignment
 ])
 def test_kv_validation(args, status):
     assert _lib.call("kv_rotate_quant4", *args) == status
@@ -130,7 +133,7 @@ def test_time_next_launch_arming():
     assert _lib.call("w4a4_time_next_launch", NUL, NUL) == _lib.W4A4_OK
     assert _lib.call("w4a4_time_next_launch", A, A + 16) == _lib.W4A4_OK
     # a failing call consumes the armed pair; nothing reads the (host) pointers
-    assert _lib.call("rotate_quant_act", A, 4, 100, 128, 128, 0, A, A, NUL, NUL) == _lib.W4A4_ERR_SHAPE
+    assert _lib.call("rotate_quant_act", A, 4, 100, 128, 128, NUL, 0, A, A, NUL, NUL) == _lib.W4A4_ERR_SHAPE
     assert _lib.call("w4a4_time_next_launch", NUL, NUL) == _lib.W4A4_OK
 
 
@@ -139,6 +142,6 @@ def test_no_device_is_a_device_error():
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    st = _lib.call("rotate_quant_act", A, 4, 128, 128, 128, 0, A, A, NUL, NUL)
+    st = _lib.call("rotate_quant_act", A, 4, 128, 128, 128, NUL, 0, A, A, NUL, NUL)
     assert st == _lib.W4A4_ERR_DEVICE
     assert "device" in _lib.last_error()
