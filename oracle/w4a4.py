@@ -367,6 +367,60 @@ def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
 
 
 # --------------------------------------------------------------------------
+# Decode attention over the rotated INT4 KV cache
+# --------------------------------------------------------------------------
+def attention_decode_f64(q, k, v, softmax_scale: float) -> np.ndarray:
+    """Textbook single-query attention per (batch, head), float64:
+    o = sum_t p_t v_t with p = softmax_t(softmax_scale * q . k_t).
+
+    q [B, H, D], k and v [B, H, S, D]; returns o [B, H, D].
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    scores = softmax_scale * np.einsum("bhd,bhsd->bhs", q, k)
+    scores -= scores.max(axis=-1, keepdims=True)
+    p = np.exp(scores)
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.einsum("bhs,bhsd->bhd", p, v)
+
+
+def kv4_attention_decode(q, k_packed, k_scale, k_zp, v_packed, v_scale, v_zp,
+                         softmax_scale: float, signs=None) -> np.ndarray:
+    """Single-query attention over a KV cache stored as rotated asymmetric INT4.
+
+    [QR] "Activation scheme": the KV cache and parts of the attention
+    computation are rotated; [ROT] "A rotation changes nothing": with an
+    orthogonal Q, (q Q) . (k Q) = q . k, so scores can be taken between the
+    rotated query and the rotated keys, and the weighted sum of rotated values
+    is rotated back once: o = o_rot Q^T.  Here Q = diag(d) H_D / sqrt(D)
+    (d = 1 without signs), the same Q the KV step used.
+
+    k_packed/v_packed [B, H, S, D/2] unsigned nibbles; k_scale/v_scale and
+    k_zp/v_zp [B, H, S] (one group per head vector); the dequantized rotated
+    vectors are scale * (code - zp) (see `dequant_asym_groups`).
+    Returns o [B, H, D] float64.
+    """
+    q = np.asarray(q, dtype=F64)
+    B, H, D = q.shape
+    S = np.asarray(k_packed).shape[2]
+
+    def deq(packed, scale, zp):
+        u = unpack_nibbles(np.asarray(packed).reshape(-1, D // 2), signed=False)
+        flat = dequant_asym_groups(u, np.asarray(scale).reshape(-1, 1), np.asarray(zp).reshape(-1, 1), D)
+        return flat.reshape(B, H, S, D)
+
+    q_rot = rotate_normalized(q.reshape(-1, D), D, signs).reshape(B, H, D)
+    o_rot = attention_decode_f64(q_rot, deq(k_packed, k_scale, k_zp), deq(v_packed, v_scale, v_zp),
+                                 softmax_scale)
+    # o = o_rot Q^T = o_rot H diag(d) / sqrt(D)   (H symmetric)
+    h = hadamard(D).astype(F64)
+    o = (o_rot.reshape(-1, D) @ h) / np.sqrt(D)
+    o = apply_signs(o, signs)
+    return o.reshape(B, H, D)
+
+
+# --------------------------------------------------------------------------
 # Statistics the rotation page measures
 # --------------------------------------------------------------------------
 def kurtosis(v) -> float:

@@ -474,3 +474,88 @@ def test_signed_rotation_lowers_int4_product_error():
     ref = x @ w.T
     e_rot = np.linalg.norm(lin["y"] - ref) / np.linalg.norm(ref)
     assert e_rot < 0.5 * e_plain
+
+
+# ---------------------------------------------------------------- decode attention over the INT4 KV cache
+def test_attention_decode_brute_force():
+    """Python loops with math.exp on a tiny case."""
+    rng = np.random.default_rng(1)
+    B, H, S, D = 1, 2, 5, 4
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, H, S, D))
+    v = rng.standard_normal((B, H, S, D))
+    o = O.attention_decode_f64(q, k, v, 0.7)
+    for h in range(H):
+        sc = [0.7 * sum(q[0, h, d] * k[0, h, t, d] for d in range(D)) for t in range(S)]
+        mx = max(sc)
+        e = [math.exp(x - mx) for x in sc]
+        z = sum(e)
+        for d in range(D):
+            want = sum(e[t] / z * v[0, h, t, d] for t in range(S))
+            assert abs(o[0, h, d] - want) < 1e-12
+
+
+def test_attention_decode_closed_forms():
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((1, 1, 9, 8))
+    v = rng.standard_normal((1, 1, 9, 8))
+    # q = 0: every score equal -> the mean of v
+    assert np.allclose(O.attention_decode_f64(np.zeros((1, 1, 8)), k, v, 1.0), v.mean(axis=2), atol=1e-14)
+    # one key far above the rest -> that key's value
+    q = np.zeros((1, 1, 8))
+    q[0, 0, 0] = 1.0
+    k2 = np.zeros_like(k)
+    k2[0, 0, 4, 0] = 1000.0
+    assert np.allclose(O.attention_decode_f64(q, k2, v, 1.0), v[:, :, 4], atol=1e-12)
+
+
+@pytest.mark.parametrize("with_signs", [False, True])
+def test_rotated_attention_invariance(with_signs):
+    """softmax((qQ)(kQ)^T) (vQ) Q^T = softmax(q k^T) v for orthogonal Q = diag(d) H / sqrt(128)."""
+    rng = np.random.default_rng(3)
+    B, H, S, D = 2, 3, 40, 128
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, H, S, D))
+    v = rng.standard_normal((B, H, S, D))
+    d = WL.hadamard_signs(D, seed=9) if with_signs else None
+    rot = lambda a: O.rotate_normalized(a.reshape(-1, D), D, d).reshape(a.shape)   # noqa: E731
+    o_rot = O.attention_decode_f64(rot(q), rot(k), rot(v), 0.125)
+    back = O.apply_signs(O.rotate_normalized(o_rot.reshape(-1, D), D), d).reshape(B, H, D)
+    assert np.max(np.abs(back - O.attention_decode_f64(q, k, v, 0.125))) < 1e-12
+
+
+@pytest.mark.parametrize("with_signs", [False, True])
+def test_kv4_attention_matches_original_domain(with_signs):
+    """kv4_attention_decode (scores and weighted sum in the rotated domain,
+    output rotated back) equals plain attention over the dequantized K and V
+    rotated back to the original domain first: checks the rotation bookkeeping."""
+    kvd = WL.kv(B=1, H=2, S=64)
+    kv = kvd["KV"]
+    vv = WL.kv(B=1, H=2, S=64)["KV"][:, :, ::-1].copy()
+    q = WL.small_random(4, 2, 128).reshape(1, 2, 128)
+    D = 128
+    d = WL.hadamard_signs(D, seed=1) if with_signs else None
+    kq = O.kv_rotate_quant(kv, signs=d)
+    vq = O.kv_rotate_quant(vv, signs=d)
+    o = O.kv4_attention_decode(q, kq["packed"], kq["scale"], kq["zp"], vq["packed"], vq["scale"], vq["zp"],
+                               1 / math.sqrt(D), signs=d)
+
+    def unrot(qd, shape):
+        u = O.unpack_nibbles(qd["packed"].reshape(-1, D // 2), signed=False)
+        yhat = O.dequant_asym_groups(u, qd["scale"].reshape(-1, 1), qd["zp"].reshape(-1, 1), D)
+        return O.apply_signs(O.rotate_normalized(yhat, D), d).reshape(shape)
+
+    want = O.attention_decode_f64(q, unrot(kq, kv.shape), unrot(vq, vv.shape), 1 / math.sqrt(D))
+    assert np.max(np.abs(o - want)) < 1e-10
+    # the rotation helps the 4-bit cache: the same asymmetric quantizer on the
+    # unrotated head vectors gives a larger attention error (outlier dims x20)
+    exact = O.attention_decode_f64(q, kv, vv, 1 / math.sqrt(D))
+
+    def plain(x):
+        g = O.quant_asym_groups(x.reshape(-1, D).astype(np.float64), 1, D)
+        return O.dequant_asym_groups(g["codes"], g["scale"], g["zp"], D).reshape(x.shape)
+
+    e_rot = np.linalg.norm(o - exact) / np.linalg.norm(exact)
+    e_plain = np.linalg.norm(O.attention_decode_f64(q, plain(kv), plain(vv), 1 / math.sqrt(D)) - exact) \
+        / np.linalg.norm(exact)
+    assert e_rot < e_plain
