@@ -205,6 +205,20 @@ def run_suite(torch, R, WL):
     emit("kv_rotate_quant4", "kv 8x32x4096x128",
          _time_kernel(torch, lambda: R.kv_rotate_quant4(kv), flush),
          nbytes=2 * kv.numel() + kv.numel() // 2 + 5 * (kv.numel() // 128))
+    # decode attention over the INT4 cache (K = the KV workload, V = its heads reversed)
+    kc, ks, kz = R.kv_rotate_quant4(kv)
+    vc, vs, vz = R.kv_rotate_quant4(kv.flip(1).contiguous())
+    q = T(WL.small_random(123, 8 * 32, 128).reshape(8, 32, 128))
+    o = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
+    emit("kv4_attention_decode", "q 8x32 over kv 8x32x4096x128 int4",
+         _time_kernel(torch, lambda: R.kv4_attention_decode(q, kc, ks, kz, vc, vs, vz, out=o), flush),
+         nbytes=attn_bytes(8, 32, 4096))
+
+
+def attn_bytes(B: int, H: int, S: int) -> int:
+    """Algorithmic bytes of one decode-attention launch: the K and V codes,
+    scales and zero-points of every cached token, the query and the output."""
+    return B * H * (S * (64 + 64 + 4 + 4 + 1 + 1) + 128 * 2 + 128 * 4)
 
 
 def run_only(torch, R, WL, which, steps, had):
@@ -244,6 +258,14 @@ def run_only(torch, R, WL, which, steps, had):
         xc, xs, xz = R.rotate_quant_act(x, 128, "asym")
         y = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
         fn = lambda: R.w4a4_gemm(xc, xs, xz, wc, ws, act_mode="asym", out=y)   # noqa: E731
+    elif which == "attn":
+        kv = T(WL.kv()["KV"])
+        kc, ks, kz = R.kv_rotate_quant4(kv)
+        vc, vs, vz = R.kv_rotate_quant4(kv.flip(1).contiguous())
+        del kv
+        q = T(WL.small_random(123, 8 * 32, 128).reshape(8, 32, 128))
+        o = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
+        fn = lambda: R.kv4_attention_decode(q, kc, ks, kz, vc, vs, vz, out=o)  # noqa: E731
     else:
         kv = T(WL.kv()["KV"])
         fn = lambda: R.kv_rotate_quant4(kv)                                    # noqa: E731
@@ -262,7 +284,7 @@ def main() -> int:
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
-    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "decode", "gateup", "downproj", "copy"],
+    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "decode", "gateup", "downproj", "copy"],
                     help="launch one kernel --steps times back to back (for rocprofv3 runs)")
     args = ap.parse_args()
 

@@ -188,6 +188,34 @@ W4A4_API w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t
                              const uint16_t* had_signs,
                              uint8_t* codes, float* scales, uint8_t* zeros, void* stream);
 
+/*
+ * kv4_attention_decode - single-query attention per (batch, head) over a KV
+ * cache that kv_rotate_quant4 stored as rotated asymmetric INT4:
+ *   o[b][h] = sum_t p_t v[b][h][t],  p = softmax_t(softmax_scale * q[b][h] . k[b][h][t]),
+ * computed without leaving the rotated domain: the query is rotated by the
+ * same Q = diag(d) H_128 / sqrt(128) as the cache, scores and the weighted
+ * value sum use the dequantized rotated vectors s (code - zero), and the
+ * result is rotated back once (o = o_rot Q^T).
+ *   Page "QuaRot (rotation-based outlier removal, W4A4KV4)", field
+ *   "Activation scheme" (the KV cache and parts of the attention computation
+ *   are rotated); page "Rotations for 4-Bit Activations: QuaRot, SpinQuant,
+ *   and Friends", section "A rotation changes nothing, and that is the point".
+ *
+ *   q_f16     [B][H][128] fp16, dense (one decode query per head).
+ *   k_codes, v_codes    [B][H][S][64], k_scales, v_scales [B][H][S] fp32,
+ *   k_zeros, v_zeros    [B][H][S] uint8: dense, as kv_rotate_quant4 writes them.
+ *   D == 128; B, H >= 0 (B*H == 0: no-op); 1 <= S < 2^25.
+ *   softmax_scale  finite, > 0 (typically 1/sqrt(128)).
+ *   had_signs NULL, or the fp16 +-1 vector [128] the cache was rotated with.
+ *   out       [B][H][128] fp32 (written).
+ * One workgroup per (b, h); every token's codes are read once.
+ */
+W4A4_API w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* k_codes,
+                             const float* k_scales, const uint8_t* k_zeros,
+                             const uint8_t* v_codes, const float* v_scales, const uint8_t* v_zeros,
+                             int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
+                             const uint16_t* had_signs, float* out, void* stream);
+
 /* Message of the last failed call on this thread ("" after a success). */
 W4A4_API const char* w4a4_last_error(void);
 

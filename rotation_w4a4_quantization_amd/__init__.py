@@ -12,6 +12,7 @@ exception.  Every step of the computation runs in the library's kernels.
     wq, ws, gsum = quant_weight_offline(w, had_block=128, signs=d)
     y = w4a4_gemm(codes, scales, zeros, wq, ws, act_mode="sym")
     kc, ks, kz = kv_rotate_quant4(kv)
+    o = kv4_attention_decode(q, kc, ks, kz, vc, vs, vz)   # decode attention on the INT4 cache
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HA
                    last_error)
 
 __all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-           "abi_version", "W4A4Error"]
+           "kv4_attention_decode", "abi_version", "W4A4Error"]
 
 _MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
 
@@ -173,3 +174,41 @@ def kv_rotate_quant4(kv: torch.Tensor, signs=None):
                    _ptr(zeros), _stream(dev))
     _check(st, "kv_rotate_quant4")
     return codes, scales, zeros
+
+
+def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
+                         softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None):
+    """Single-query attention per (batch, head) over a KV cache written by
+    kv_rotate_quant4 (rotated asymmetric INT4); q fp16 [B, H, 128].
+
+    softmax_scale defaults to 1/sqrt(128); signs is the fp16 +-1 vector the
+    cache was rotated with (None: plain Hadamard).  Returns fp32 [B, H, 128].
+    """
+    _need(q, torch.float16, "q")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, D] tensor")
+    B, H, D = q.shape
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (v_codes, "v_codes", torch.uint8),
+                     (k_scales, "k_scales", torch.float32), (v_scales, "v_scales", torch.float32),
+                     (k_zeros, "k_zeros", torch.uint8), (v_zeros, "v_zeros", torch.uint8)):
+        _need(t, dt, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if k_codes.dim() != 4 or tuple(k_codes.shape[:2]) != (B, H) or tuple(v_codes.shape) != tuple(k_codes.shape):
+        raise ValueError("k_codes and v_codes must both be [B, H, S, D/2]")
+    S = k_codes.shape[2]
+    for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales"), (k_zeros, "k_zeros"), (v_zeros, "v_zeros")):
+        if tuple(t.shape) != (B, H, S):
+            raise ValueError(f"{n} must be [B, H, S]")
+    dev = q.device
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / (D ** 0.5)
+    y = out if out is not None else torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _need(y, torch.float32, "out")
+    if tuple(y.shape) != (B, H, D) or not y.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, D] fp32 tensor")
+    sg = _signs(signs, D, dev)
+    st = _lib.call("kv4_attention_decode", _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),
+                   _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), B, H, S, D, scale, _ptr(sg), _ptr(y),
+                   _stream(dev))
+    _check(st, "kv4_attention_decode")
+    return y

@@ -26,6 +26,8 @@ SIGNATURES = {
     "w4a4_gemm": [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "kv_rotate_quant4": [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "w4a4_time_next_launch": [_vp, _vp],
+    "kv4_attention_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                             _vp, _vp, _vp],
 }
 
 _lib = None

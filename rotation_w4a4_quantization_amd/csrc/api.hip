@@ -273,4 +273,43 @@ w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t H, int64
                   "kv_rotate_quant4");
 }
 
+w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* k_codes, const float* k_scales,
+                                 const uint8_t* k_zeros, const uint8_t* v_codes, const float* v_scales,
+                                 const uint8_t* v_zeros, int64_t B, int64_t H, int64_t S, int64_t D,
+                                 float softmax_scale, const uint16_t* had_signs, float* out,
+                                 void* stream) {
+  TimingScope timing_scope;
+  if (D != 128) return fail(W4A4_ERR_SHAPE, "D=%lld must be 128", (long long)D);
+  if (B < 0 || H < 0) return fail(W4A4_ERR_SHAPE, "B and H must be >= 0");
+  if (S < 1 || S >= (int64_t(1) << 25)) return fail(W4A4_ERR_SHAPE, "S=%lld must be in [1, 2^25)", (long long)S);
+  if (H >= (int64_t(1) << 31) || (B > 0 && B * H >= (int64_t(1) << 31)))
+    return fail(W4A4_ERR_SHAPE, "B*H must be < 2^31");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(W4A4_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  const int64_t bh = B * H;
+  if (bh == 0) return ok();   // nothing is read or written: pointers may be NULL
+  if (!q_f16 || !k_codes || !k_scales || !k_zeros || !v_codes || !v_scales || !v_zeros || !out)
+    return fail(W4A4_ERR_NULL, "q, the K and V codes, scales and zeros, and out must be non-NULL");
+  if (!aligned16(q_f16) || !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_zeros) ||
+      !aligned16(v_codes) || !aligned16(v_scales) || !aligned16(v_zeros) || !aligned16(out) ||
+      (had_signs && !aligned16(had_signs)))
+    return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  if (w4a4_status s = check_device()) return s;
+
+  w4a4::AttnParams p{};
+  p.q = q_f16;
+  p.k_codes = k_codes;
+  p.k_scales = k_scales;
+  p.k_zeros = k_zeros;
+  p.v_codes = v_codes;
+  p.v_scales = v_scales;
+  p.v_zeros = v_zeros;
+  p.signs = had_signs;
+  p.out = out;
+  p.BH = bh;
+  p.S = S;
+  p.scale2 = (float)((double)softmax_scale * 1.4426950408889634);
+  return launched(w4a4::launch_kv4_attention(p, (hipStream_t)stream), "kv4_attention_decode");
+}
+
 }  // extern "C"

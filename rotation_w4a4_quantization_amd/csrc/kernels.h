@@ -53,6 +53,23 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st);
 hipError_t gemm_prepare_device();   // once per device, before the first GEMM launch
 
+// Decode attention over the rotated INT4 KV cache (one query per head).
+struct AttnParams {
+  const uint16_t* q;          // [BH][128] fp16
+  const uint8_t* k_codes;     // [BH][S][64]
+  const float* k_scales;      // [BH][S]
+  const uint8_t* k_zeros;     // [BH][S]
+  const uint8_t* v_codes;
+  const float* v_scales;
+  const uint8_t* v_zeros;
+  const uint16_t* signs;      // optional [128] fp16 +-1
+  float* out;                 // [BH][128] fp32
+  int64_t BH, S;
+  float scale2;               // softmax scale * log2(e)
+};
+
+hipError_t launch_kv4_attention(const AttnParams& p, hipStream_t st);
+
 // Optional per-launch timing: events armed on this host thread are attached to
 // the next kernel launch (the runtime writes the kernel's own start and end
 // timestamps into them) and then disarmed.

@@ -20,7 +20,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-              "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch"):
+              "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode"):
         assert n in names
 
 
@@ -123,6 +123,26 @@ def test_gemm_validation(args, status):
 ])
 def test_kv_validation(args, status):
     assert _lib.call("kv_rotate_quant4", *args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, kc, ks, kz, vc, vs, vz, B, H, S, D, scale, signs, out, stream
+    ((NUL, A, A, A, A, A, A, 1, 2, 16, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, A, A, NUL, 1, 2, 16, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, A, A, A, 1, 2, 16, 128, 0.1, NUL, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, A, A, A, 1, 2, 16, 64, 0.1, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),     # D != 128
+    ((A, A, A, A, A, A, A, 1, 2, 0, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),     # S == 0
+    ((A, A, A, A, A, A, A, 1, 2, 1 << 25, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A, A, A, A, A, A, -1, 2, 16, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A, A, A, A, A, A, 1, 2, 16, 128, 0.0, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),    # scale <= 0
+    ((A, A, A, A, A, A, A, 1, 2, 16, 128, float("nan"), NUL, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A + 4, A, A, A, A, A, A, 1, 2, 16, 128, 0.1, NUL, A, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, A, A, A, A, A, A, 1, 2, 16, 128, 0.1, A + 2, A, NUL), _lib.W4A4_ERR_ALIGN),  # signs
+    ((A, A, A, A, A, A, A, 0, 2, 16, 128, 0.1, NUL, A, NUL), _lib.W4A4_OK),           # B*H == 0
+    ((NUL, NUL, NUL, NUL, NUL, NUL, NUL, 3, 0, 16, 128, 0.1, NUL, NUL, NUL), _lib.W4A4_OK),
+])
+def test_kv4_attention_validation(args, status):
+    assert _lib.call("kv4_attention_decode", *args) == status
 
 
 def test_time_next_launch_arming():
