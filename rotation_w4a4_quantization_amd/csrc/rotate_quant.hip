@@ -110,7 +110,7 @@ __device__ __forceinline__ uint32_t pack8(const uint32_t* b) {
 
 }  // namespace
 
-template <int MODE, int LOG_NB_FULL, bool GSUM, bool STRIDED>
+template <int MODE, int LOG_NB_FULL, bool GSUM, bool STRIDED, bool SIGNS>
 __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
@@ -130,10 +130,10 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
 
   // randomized Hadamard: the diagonal D depends on the column only, so each
   // lane loads the sign bits of its 32 columns once and flips its inputs'
-  // signs (one XOR per pair of fp16 values) before the transform
-  const bool has_signs = p.signs != nullptr;
+  // signs (one XOR per pair of fp16 values) before the transform.  A
+  // separate instantiation, so the plain rotation keeps its registers.
   uint4 sg[4] = {};
-  if (has_signs) {
+  if constexpr (SIGNS) {
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
         (void*)p.signs, (short)0, p.K * 2, 0x00020000);
     const uint32_t soff = lane_ok ? (uint32_t)((blk * 128 + q * 8) * 2) : 0x7FFFFFF0u;
@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
         w[r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_off, 64 * r4, 0));
     }
 
-    if (has_signs) {
+    if constexpr (SIGNS) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         w[r4].x ^= sg[r4].x;
@@ -323,8 +323,12 @@ namespace {
 
 template <int MODE, int LOGF, bool GSUM, bool STRIDED>
 hipError_t launch_t(const RQParams& p, int threads, size_t lds, int64_t grid, hipStream_t st) {
-  W4A4_LAUNCH((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED>), dim3((uint32_t)grid),
-              dim3(threads), lds, st, p);
+  if (p.signs)
+    W4A4_LAUNCH((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED, true>), dim3((uint32_t)grid),
+                dim3(threads), lds, st, p);
+  else
+    W4A4_LAUNCH((rotate_quant_kernel<MODE, LOGF, GSUM, STRIDED, false>), dim3((uint32_t)grid),
+                dim3(threads), lds, st, p);
   return hipGetLastError();
 }
 
