@@ -367,6 +367,101 @@ def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
 
 
 # --------------------------------------------------------------------------
+# MXFP4: E2M1 elements with a power-of-two scale shared by 32 values
+# --------------------------------------------------------------------------
+# [ROT] "Gotchas" / "When to rotate": MXFP4 is a 4-bit format whose scales
+# are powers of two shared by 32 values, and rotations help it (unlike
+# NVFP4).  Reading (the pages give no formulas; this is the usual MX
+# convention): the element grid is E2M1, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
+# for codes 0..7 with bit 3 the sign; the shared scale of a block is
+# 2^e, e = floor(log2(max|y|)) - 2 (2 = the exponent of E2M1's largest value),
+# stored as the biased byte e + 127; elements round to nearest on the grid,
+# ties to the even code, and saturate at +-6.  A block of zeros gets the
+# byte 0 and zero codes.  What is quantized is the normalized rotated value
+# y = x Q (the scale is a power of two, so 1/sqrt(b) matters here), formed in
+# fp32 as the kernel forms it: y = fl32(fl32(z) * fl32(1/sqrt(b))).
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_BLOCK = 32
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """Decode 4-bit E2M1 codes (bit 3 = sign) to float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = E2M1[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_round(t) -> np.ndarray:
+    """Nearest E2M1 code of each value (ties to the even code, saturating at 6).
+
+    Written out as the distance to every grid point; among equally near
+    points the one with an even code wins.
+    """
+    t = np.asarray(t, dtype=F64)
+    a = np.minimum(np.abs(t), 6.0)
+    d = np.abs(a[..., None] - E2M1)                        # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # prefer the even code among the nearest (codes are 0..7 in grid order)
+    even = cand & ((np.arange(8) % 2) == 0)
+    pick = np.where(even.any(axis=-1, keepdims=True), even, cand)
+    mag = np.argmax(pick, axis=-1)
+    neg = (t < 0) & (mag > 0)
+    return (mag + 8 * neg).astype(np.int64)
+
+
+def mx_quant_rows(y32, block: int = MX_BLOCK) -> dict:
+    """MXFP4 quantization of fp32 rows y32 [R, K] in blocks of 32 along K.
+
+    Returns codes [R, K] (0..15), scale_e [R, K/32] (the exponent e) and
+    scale_byte (e + 127).
+    """
+    y = np.asarray(y32, dtype=F32).astype(F64)
+    R, K = y.shape
+    yb = y.reshape(R, K // block, block)
+    amax = np.abs(yb).max(axis=-1)
+    mant, ex = np.frexp(amax)                              # amax = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127)               # floor(log2 amax) - 2
+    e = np.clip(e, -127, 127).astype(np.int64)
+    t = yb / np.exp2(e.astype(F64))[..., None]             # exact: division by a power of two
+    codes = e2m1_round(t).reshape(R, K)
+    return dict(codes=codes, scale_e=e, scale_byte=(e + 127).astype(np.uint8))
+
+
+def mx_dequant_rows(codes, scale_e, block: int = MX_BLOCK) -> np.ndarray:
+    c = np.asarray(codes)
+    R, K = c.shape
+    v = e2m1_value(c).reshape(R, K // block, block)
+    return (v * np.exp2(np.asarray(scale_e, dtype=F64))[..., None]).reshape(R, K)
+
+
+def rotate_mx_quant(x, block: int, signs=None) -> dict:
+    """Rotate each row (Q = diag(d) H_block / sqrt(block)), then MXFP4.
+
+    [ROT] "Gotchas": rotations help MXFP4, whose scales are powers of two
+    shared by 32 values.  Codes are packed two per byte like the INT4 codes.
+    """
+    z = rotate(x, block, signs)
+    y32 = (z.astype(F32) * F32(1.0 / np.sqrt(block))).astype(F32)
+    d = mx_quant_rows(y32)
+    d["packed"] = pack_nibbles(d["codes"])
+    d["y32"] = y32
+    return d
+
+
+def mx_gemm_f64(ca, ea, cb, eb, block: int = MX_BLOCK) -> np.ndarray:
+    """Y[m, n] = sum over 32-blocks j of 2^(ea[m,j] + eb[n,j]) * sum_{k in j} a[m,k] b[n,k],
+    in float64 (every term is a dyadic rational; exact for these sizes)."""
+    va = e2m1_value(ca)
+    vb = e2m1_value(cb)
+    M, K = va.shape
+    N = vb.shape[0]
+    J = K // block
+    part = np.einsum("mjk,njk->mnj", va.reshape(M, J, block), vb.reshape(N, J, block))
+    return np.einsum("mnj,mnj->mn", part, np.exp2(np.asarray(ea, F64)[:, None, :] + np.asarray(eb, F64)[None, :, :]))
+
+
+# --------------------------------------------------------------------------
 # Decode attention over the rotated INT4 KV cache
 # --------------------------------------------------------------------------
 def attention_decode_f64(q, k, v, softmax_scale: float) -> np.ndarray:

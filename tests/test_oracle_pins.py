@@ -559,3 +559,106 @@ def test_kv4_attention_matches_original_domain(with_signs):
     e_plain = np.linalg.norm(O.attention_decode_f64(q, plain(kv), plain(vv), 1 / math.sqrt(D)) - exact) \
         / np.linalg.norm(exact)
     assert e_rot < e_plain
+
+
+# ---------------------------------------------------------------- MXFP4 (E2M1 + power-of-two scale per 32)
+def _e2m1_from_bits(c):
+    """E2M1 from its bit fields: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0;
+    exponent 0 is subnormal (0.5 m)."""
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return -mag if s else mag
+
+
+def test_e2m1_decode_matches_bit_fields():
+    for c in range(16):
+        assert O.e2m1_value([c])[0] == float(_e2m1_from_bits(c))
+
+
+def test_e2m1_round_brute_force():
+    """Every multiple of 1/8 in [-8, 8]: nearest representable value, ties to the
+    even mantissa, saturation at +-6, no negative zero."""
+    values = [Fraction(i, 8) for i in range(-64, 65)]
+    codes = O.e2m1_round([float(v) for v in values])
+    grid = [(c, _e2m1_from_bits(c)) for c in range(8)]
+    for v, got in zip(values, codes):
+        a = min(abs(v), Fraction(6))
+        best = min(abs(a - g) for _, g in grid)
+        near = [c for c, g in grid if abs(a - g) == best]
+        c = near[0] if len(near) == 1 else [c for c in near if c % 2 == 0][0]
+        want = c + (8 if v < 0 and c > 0 else 0)
+        assert got == want, (v, got, want)
+
+
+def test_mx_scale_worked_examples():
+    """Hand-worked blocks: amax 6 -> e = 0 (6 exact); amax 3 -> e = -1 (3 -> 6, 1 -> 2);
+    amax 0.3 -> floor(log2 0.3) = -2, e = -4, 0.3 * 16 = 4.8 -> nearest 4 (code 6);
+    amax 7 -> e = 0 and 7 saturates to 6; a zero block -> byte 0, codes 0."""
+    y = np.zeros((5, 32), np.float32)
+    y[0, 0], y[0, 1] = 6.0, -0.5
+    y[1, 0], y[1, 1] = 3.0, 1.0
+    y[2, 0] = 0.3
+    y[3, 0] = 7.0
+    q = O.mx_quant_rows(y)
+    assert list(q["scale_e"][:, 0]) == [0, -1, -4, 0, -127]
+    assert list(q["scale_byte"][:, 0]) == [127, 126, 123, 127, 0]
+    assert (q["codes"][0, 0], q["codes"][0, 1]) == (7, 9)
+    assert (q["codes"][1, 0], q["codes"][1, 1]) == (7, 4)
+    assert q["codes"][2, 0] == 6 and q["codes"][3, 0] == 7
+    assert np.all(q["codes"][4] == 0)
+
+
+def test_mx_quant_invariants():
+    y = WL.small_random(31, 64, 256, outlier_cols=(7,), mult=50.0).astype(np.float32)
+    q = O.mx_quant_rows(y)
+    deq = O.mx_dequant_rows(q["codes"], q["scale_e"])
+    yb = y.astype(np.float64).reshape(64, 8, 32)
+    scale = np.exp2(q["scale_e"].astype(np.float64))[..., None]
+    t = np.abs(yb) / scale
+    # up to 6 * 2^e the error is at most half the local grid step; above it
+    # (the block maximum lands in [4, 8), so values in (6, 8) exist) the value
+    # saturates to +-6 * 2^e
+    deq = deq.reshape(64, 8, 32)
+    step = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
+    inside = t <= 6
+    assert np.all(np.abs(deq - yb)[inside] <= (step * scale / 2)[inside])
+    assert np.all(np.abs(deq)[~inside] == (6 * scale * np.ones_like(t))[~inside])
+    amax_t = t.max(axis=-1)
+    assert np.all((amax_t >= 4) & (amax_t < 8))
+
+
+def test_mx_gemm_brute_force():
+    rng = np.random.default_rng(5)
+    ca = rng.integers(0, 16, (3, 64))
+    cb = rng.integers(0, 16, (2, 64))
+    ea = rng.integers(-6, 6, (3, 2))
+    eb = rng.integers(-6, 6, (2, 2))
+    y = O.mx_gemm_f64(ca, ea, cb, eb)
+    for m in range(3):
+        for n in range(2):
+            acc = Fraction(0)
+            for k in range(64):
+                j = k // 32
+                acc += _e2m1_from_bits(int(ca[m, k])) * _e2m1_from_bits(int(cb[n, k])) \
+                    * Fraction(2) ** int(ea[m, j] + eb[n, j])
+            assert y[m, n] == float(acc)
+
+
+def test_rotation_lowers_mxfp4_product_error():
+    """[ROT] "Gotchas": rotations help MXFP4 -- q_proj-like fixed outlier channels."""
+    d = WL.qproj(M=256, with_w=False)
+    x = d["X"].astype(np.float64)
+    w = WL.qproj_weight()[:256].astype(np.float64)
+    ref = x @ w.T
+
+    def err(xq, wq):
+        return np.linalg.norm(xq @ wq.T - ref) / np.linalg.norm(ref)
+
+    plain = err(O.mx_dequant_rows(**{k: v for k, v in O.mx_quant_rows(x.astype(np.float32)).items()
+                                     if k in ("codes", "scale_e")}),
+                O.mx_dequant_rows(**{k: v for k, v in O.mx_quant_rows(w.astype(np.float32)).items()
+                                     if k in ("codes", "scale_e")}))
+    for block in (128, 4096):
+        qa, qw = O.rotate_mx_quant(x, block), O.rotate_mx_quant(w, block)
+        rot = err(O.mx_dequant_rows(qa["codes"], qa["scale_e"]), O.mx_dequant_rows(qw["codes"], qw["scale_e"]))
+        assert rot < plain, (block, rot, plain)
