@@ -84,10 +84,10 @@ typedef enum {
 enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
 enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
 
-#define W4A4_ABI_VERSION 2
+#define W4A4_ABI_VERSION 3
 
 /*
- * had_signs (the three rotate calls): NULL, or a device array of K fp16
+ * had_signs (the four rotate calls): NULL, or a device array of K fp16
  * values (D = 128 for kv_rotate_quant4), each +1.0 or -1.0, 16-byte aligned.
  * Non-NULL turns the rotation into the randomized Hadamard Q = diag(d) H / sqrt(b):
  * element k of every row is multiplied by d[k] (its sign bit is flipped
@@ -215,6 +215,54 @@ W4A4_API w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* 
                              const uint8_t* v_codes, const float* v_scales, const uint8_t* v_zeros,
                              int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
                              const uint16_t* had_signs, float* out, void* stream);
+
+/*
+ * rotate_quant_mxfp4 - the rotate step with MXFP4 output: per row, the same
+ * normalized Hadamard as rotate_quant_act (per 128-block or full width,
+ * optionally randomized), then every 32 consecutive values share one
+ * power-of-two scale and become E2M1 codes.  Serves activations online and
+ * weights offline alike (both operands of mxfp4_gemm).
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   sections "The full model in NVFP4, on vLLM" and "When to rotate"
+ *   (rotations help MXFP4: 4-bit values with a power-of-two scale per 32).
+ *   The pages give no formulas; the conversion is the usual MX one:
+ *     y = fl32(fl32(z) * fl32(1/sqrt(b))), z = the unnormalized transform;
+ *     e = floor(log2(max |y| over the 32)) - 2, clamped to [-127, 127]
+ *         (a block of zeros: e = -127);
+ *     code = E2M1 nearest to y / 2^e (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+ *            for codes 0..7, bit 3 = sign, ties to the even code,
+ *            saturating at 6, no negative zero).
+ *
+ *   x_f16, M, K, ldx, had_block as in rotate_quant_act (had_block
+ *   W4A4_HAD_FULL needs K a power of two).
+ *   codes        [M][K/2] packed, element 2i in the low nibble of byte i (written).
+ *   scales_e8m0  [M][K/32] uint8 biased exponents e + 127 (written).
+ */
+W4A4_API w4a4_status rotate_quant_mxfp4(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
+                               int32_t had_block, const uint16_t* had_signs, uint8_t* codes,
+                               uint8_t* scales_e8m0, void* stream);
+
+/*
+ * mxfp4_gemm - Y = dequant(X) . dequant(W)^T for MXFP4 operands, on
+ * gfx950's block-scaled FP4 matrix instruction:
+ *   Y[m][n] = sum_j 2^(ex[m][j] + ew[n][j]) * sum_{k in 32-block j} a[m][k] b[n][k],
+ * a, b the E2M1 values of the codes, e = scale byte - 127; accumulated in
+ * fp32 (the result agrees with the exact sum to fp32 rounding).
+ *   Same pages and sections as rotate_quant_mxfp4; page "Rotations for
+ *   4-Bit Activations: QuaRot, SpinQuant, and Friends", section "A rotation
+ *   changes nothing, and that is the point" (the product of the rotated
+ *   operands is X W^T).
+ *
+ *   x_codes [M][K/2], x_scales_e8m0 [M][K/32]; w_codes [N][K/2],
+ *   w_scales_e8m0 [N][K/32], as rotate_quant_mxfp4 writes them; scale
+ *   byte 255 (not produced by the quantizer) gives NaN.
+ *   y [M][ldy] fp32 (written).
+ *   M >= 0, N >= 1, K >= 128, K % 128 == 0, K <= 131072, ldy >= N.
+ *   M <= 16 uses a weight-streaming kernel, larger M the tiled kernel.
+ */
+W4A4_API w4a4_status mxfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scales_e8m0,
+                       const uint8_t* w_codes, const uint8_t* w_scales_e8m0,
+                       int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, void* stream);
 
 /* Message of the last failed call on this thread ("" after a success). */
 W4A4_API const char* w4a4_last_error(void);

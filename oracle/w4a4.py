@@ -369,7 +369,7 @@ def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
 # --------------------------------------------------------------------------
 # MXFP4: E2M1 elements with a power-of-two scale shared by 32 values
 # --------------------------------------------------------------------------
-# [ROT] "Gotchas" / "When to rotate": MXFP4 is a 4-bit format whose scales
+# [ROT] "The full model in NVFP4, on vLLM" / "When to rotate": MXFP4 is a 4-bit format whose scales
 # are powers of two shared by 32 values, and rotations help it (unlike
 # NVFP4).  Reading (the pages give no formulas; this is the usual MX
 # convention): the element grid is E2M1, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
@@ -438,8 +438,8 @@ def mx_dequant_rows(codes, scale_e, block: int = MX_BLOCK) -> np.ndarray:
 def rotate_mx_quant(x, block: int, signs=None) -> dict:
     """Rotate each row (Q = diag(d) H_block / sqrt(block)), then MXFP4.
 
-    [ROT] "Gotchas": rotations help MXFP4, whose scales are powers of two
-    shared by 32 values.  Codes are packed two per byte like the INT4 codes.
+    [ROT] "The full model in NVFP4, on vLLM" and "When to rotate": rotations
+    help MXFP4, whose scales are powers of two shared by 32 values.  Codes are packed two per byte like the INT4 codes.
     """
     z = rotate(x, block, signs)
     y32 = (z.astype(F32) * F32(1.0 / np.sqrt(block))).astype(F32)

@@ -13,6 +13,10 @@ exception.  Every step of the computation runs in the library's kernels.
     y = w4a4_gemm(codes, scales, zeros, wq, ws, act_mode="sym")
     kc, ks, kz = kv_rotate_quant4(kv)
     o = kv4_attention_decode(q, kc, ks, kz, vc, vs, vz)   # decode attention on the INT4 cache
+    # MXFP4 (E2M1 codes, a power-of-two scale per 32) on the scaled FP4 MFMA
+    xc, xe = rotate_quant_mxfp4(x, had_block=128)
+    wc, we = rotate_quant_mxfp4(w, had_block=128)
+    y = mxfp4_gemm(xc, xe, wc, we)
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HA
                    last_error)
 
 __all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-           "kv4_attention_decode", "abi_version", "W4A4Error"]
+           "kv4_attention_decode", "rotate_quant_mxfp4", "mxfp4_gemm", "abi_version", "W4A4Error"]
 
 _MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
 
@@ -211,4 +215,53 @@ def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v
                    _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), B, H, S, D, scale, _ptr(sg), _ptr(y),
                    _stream(dev))
     _check(st, "kv4_attention_decode")
+    return y
+
+
+def _had(had_block, K: int) -> int:
+    return W4A4_HAD_128 if had_block == 128 else (W4A4_HAD_FULL if had_block in (0, K, "full") else -1)
+
+
+def rotate_quant_mxfp4(x: torch.Tensor, had_block: int = 128, signs=None):
+    """Rotate every row of fp16 X [M, K] (activations or weights) and quantize
+    it to MXFP4: E2M1 codes with one power-of-two scale per 32 values.
+
+    Returns (codes uint8 [M, K/2], scales uint8 [M, K/32] = exponent + 127).
+    """
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    M, K = x.shape
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    sg = _signs(signs, K, dev)
+    st = _lib.call("rotate_quant_mxfp4", _ptr(x), M, K, x.stride(0), _had(had_block, K), _ptr(sg),
+                   _ptr(codes), _ptr(scales), _stream(dev))
+    _check(st, "rotate_quant_mxfp4")
+    return codes, scales
+
+
+def mxfp4_gemm(x_codes, x_scales, w_codes, w_scales, out: torch.Tensor | None = None):
+    """Y fp32 [M, N] from MXFP4 activations and weights (see include/w4a4.h)."""
+    for t, n in ((x_codes, "x_codes"), (w_codes, "w_codes"), (x_scales, "x_scales"),
+                 (w_scales, "w_scales")):
+        _need(t, torch.uint8, n)
+        if not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{n} must be a contiguous 2-D tensor")
+    M, K2 = x_codes.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K2:
+        raise ValueError("x_codes and w_codes disagree on K")
+    K = 2 * K2
+    if tuple(x_scales.shape) != (M, K // 32) or tuple(w_scales.shape) != (N, K // 32):
+        raise ValueError("scales must be [rows, K/32]")
+    dev = x_codes.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(y, torch.float32, "out")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] != N or y.stride(1) != 1:
+        raise ValueError("out must be [M, N] with contiguous rows")
+    st = _lib.call("mxfp4_gemm", _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales), M, N, K,
+                   _ptr(y), y.stride(0), _stream(dev))
+    _check(st, "mxfp4_gemm")
     return y

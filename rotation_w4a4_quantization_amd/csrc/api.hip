@@ -187,6 +187,67 @@ w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, in
                   "quant_weight_offline");
 }
 
+w4a4_status rotate_quant_mxfp4(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
+                               int32_t had_block, const uint16_t* had_signs, uint8_t* codes,
+                               uint8_t* scales_e8m0, void* stream) {
+  TimingScope timing_scope;
+  if (had_block != W4A4_HAD_FULL && had_block != W4A4_HAD_128)
+    return fail(W4A4_ERR_MODE, "had_block=%d is not W4A4_HAD_FULL or W4A4_HAD_128", had_block);
+  if (w4a4_status s = check_rows_k(M, K, ldx, "M", "ldx")) return s;
+  if (had_block == W4A4_HAD_FULL && !pow2(K))
+    return fail(W4A4_ERR_SHAPE, "full-width Hadamard needs K a power of two, got K=%lld", (long long)K);
+  if (M == 0) return ok();   // nothing is read or written: pointers may be NULL
+  if (!x_f16 || !codes || !scales_e8m0) return fail(W4A4_ERR_NULL, "x_f16, codes and scales_e8m0 must be non-NULL");
+  if (!aligned16(x_f16) || !aligned16(codes) || !aligned16(scales_e8m0) || (had_signs && !aligned16(had_signs)))
+    return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  if (w4a4_status s = check_device()) return s;
+
+  w4a4::RQParams p{};
+  p.x = x_f16;
+  p.signs = had_signs;
+  p.codes = codes;
+  p.mx_scales = scales_e8m0;
+  p.rows = M;
+  p.ss = ldx;
+  p.K = (int32_t)K;
+  p.cdiv = (float)(1.0 / std::sqrt((double)(had_block == W4A4_HAD_FULL ? K : 128)));
+  return launched(w4a4::launch_rotate_quant(p, w4a4::kModeMx, had_block == W4A4_HAD_FULL, false, false,
+                                            (hipStream_t)stream),
+                  "rotate_quant_mxfp4");
+}
+
+w4a4_status mxfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scales_e8m0, const uint8_t* w_codes,
+                       const uint8_t* w_scales_e8m0, int64_t M, int64_t N, int64_t K, float* y,
+                       int64_t ldy, void* stream) {
+  TimingScope timing_scope;
+  if (M < 0 || M >= (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "M=%lld out of range [0, 2^31)", (long long)M);
+  if (N < 1 || N >= (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "N=%lld out of range [1, 2^31)", (long long)N);
+  if (K < 128 || K % 128 != 0 || K > 131072)
+    return fail(W4A4_ERR_SHAPE, "K=%lld must be a multiple of 128 in [128, 131072]", (long long)K);
+  if (ldy < N) return fail(W4A4_ERR_SHAPE, "ldy=%lld must be >= N=%lld", (long long)ldy, (long long)N);
+  if (((M + 63) / 64) * ((N + 127) / 128) >= (int64_t(1) << 31))
+    return fail(W4A4_ERR_SHAPE, "M x N is too large for one launch");
+  if (M == 0) return ok();   // nothing is read or written: pointers may be NULL
+  if (!x_codes || !x_scales_e8m0 || !w_codes || !w_scales_e8m0 || !y)
+    return fail(W4A4_ERR_NULL, "x_codes, x_scales_e8m0, w_codes, w_scales_e8m0 and y must be non-NULL");
+  if (!aligned16(x_codes) || !aligned16(x_scales_e8m0) || !aligned16(w_codes) || !aligned16(w_scales_e8m0) ||
+      !aligned16(y))
+    return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  if (w4a4_status s = check_device()) return s;
+
+  w4a4::MxGemmParams p{};
+  p.xq = x_codes;
+  p.xe = x_scales_e8m0;
+  p.wq = w_codes;
+  p.we = w_scales_e8m0;
+  p.y = y;
+  p.M = M;
+  p.N = N;
+  p.ldy = ldy;
+  p.K = (int32_t)K;
+  return launched(w4a4::launch_mx_gemm(p, (hipStream_t)stream), "mxfp4_gemm");
+}
+
 w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, const uint8_t* x_zeros,
                       int32_t act_mode, const uint8_t* w_codes, const float* w_scales,
                       const int32_t* w_gsum, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy,

@@ -19,30 +19,13 @@
 // 16x factor leaves 16 * A_g in the accumulator.
 #include "common.h"
 #include "kernels.h"
+#include "tile.h"
 
 namespace w4a4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 namespace {
-
-// Tile coordinates of this workgroup.  Tiles are walked in groups of 16 tile
-// rows, column by column inside a group, so the workgroups resident at one
-// time cover a 16-row block of tiles and share both its A rows and its B
-// rows in L2 (row-major order would stream every B tile once per pair of
-// tile rows); measured 2-5% faster on the q_proj, down_proj and gate/up
-// shapes.  The mapping is a bijection of [0, tiles_m * tiles_n).
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  constexpr int64_t GM = 16;
-  const int64_t pid = blockIdx.x;
-  const int64_t in_group = GM * tiles_n;
-  const int64_t gid = pid / in_group;
-  const int64_t first_m = gid * GM;
-  const int64_t gsz = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-  const int64_t r = pid - gid * in_group;
-  tm = first_m + r % gsz;
-  tn = r / gsz;
-}
 
 constexpr int BN = 128, BK = 128;   // BK in 4-bit elements
 constexpr int LROW = 128;                      // LDS bytes per int8 row (one K step)
@@ -63,41 +46,6 @@ __device__ __forceinline__ void widen_signed(uint32_t p, uint32_t& even16, uint3
 
 __device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-// 16-byte output store marked non-temporal: the fp32 result is written once
-// and not re-read by this kernel, so it should not displace the operand rows
-// that other tiles still read from L2 / MALL (measured 3-15% faster).
-__device__ __forceinline__ void store_stream4(float* dst, const float* y) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(v4f{y[0], y[1], y[2], y[3]}, reinterpret_cast<v4f*>(dst));
-}
-
-// 4x4 transpose inside a quad of lanes: on entry lane k of the quad holds
-// column k of a 4x4 block in y[0..3] (y[v] = row v); on exit it holds row k
-// (y[c] = column c).  Two butterflies swap a lane-index bit with a
-// register-index bit (DPP quad permutes).
-__device__ __forceinline__ void quad_transpose4(float* y, int k) {
-  {
-    const bool hi = k & 1;
-#pragma unroll
-    for (int m = 0; m < 4; m += 2) {
-      const float send = hi ? y[m] : y[m + 1];
-      const float recv = dpp_f<0xB1>(send);
-      y[m] = hi ? recv : y[m];
-      y[m + 1] = hi ? y[m + 1] : recv;
-    }
-  }
-  {
-    const bool hi = k & 2;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const float send = hi ? y[m] : y[m + 2];
-      const float recv = dpp_f<0x4E>(send);
-      y[m] = hi ? recv : y[m];
-      y[m + 2] = hi ? y[m + 2] : recv;
-    }
-  }
 }
 
 }  // namespace

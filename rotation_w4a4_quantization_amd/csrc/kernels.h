@@ -7,7 +7,7 @@
 
 namespace w4a4 {
 
-enum { kModeSym = 0, kModeAsym = 1 };
+enum { kModeSym = 0, kModeAsym = 1, kModeMx = 2 };
 
 // Rotate + quantize: one row of K fp16 values -> K/2 code bytes.
 struct RQParams {
@@ -16,6 +16,7 @@ struct RQParams {
   uint8_t* codes;    // [rows][K/2]
   float* scales;     // sym: [rows]; asym: [rows][K/128]
   uint8_t* zeros;    // asym: [rows][K/128]
+  uint8_t* mx_scales;  // MXFP4: [rows][K/32] biased power-of-two exponents
   int32_t* gsum;     // optional: [rows][K/128]
   int64_t rows;
   int64_t ss;        // row stride in elements (strided mode: the s stride)
@@ -26,7 +27,7 @@ struct RQParams {
   int32_t seg;       // threads per row slot (set by the launcher)
   int32_t rows_per_wg;
   int32_t log2seg;   // log2(seg) when rows_per_wg > 1
-  float cdiv;        // fl32(7 sqrt(b)) (sym) or fl32(15 sqrt(b)) (asym)
+  float cdiv;        // fl32(7 sqrt(b)) (sym), fl32(15 sqrt(b)) (asym), fl32(1 / sqrt(b)) (MXFP4)
 };
 
 struct RQGeometry {
@@ -52,6 +53,19 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st);
 hipError_t gemm_prepare_device();   // once per device, before the first GEMM launch
+
+// MXFP4 GEMM: Y = sum over 32-blocks of 2^(ea + eb) * (E2M1 codes . E2M1 codes).
+struct MxGemmParams {
+  const uint8_t* xq;    // [M][K/2] packed E2M1 codes
+  const uint8_t* xe;    // [M][K/32] biased exponents
+  const uint8_t* wq;    // [N][K/2]
+  const uint8_t* we;    // [N][K/32]
+  float* y;
+  int64_t M, N, ldy;
+  int32_t K;
+};
+
+hipError_t launch_mx_gemm(const MxGemmParams& p, hipStream_t st);
 
 // Decode attention over the rotated INT4 KV cache (one query per head).
 struct AttnParams {

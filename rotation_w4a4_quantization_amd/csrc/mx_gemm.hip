@@ -1,0 +1,325 @@
+// MXFP4 GEMM on gfx950's block-scaled FP4 MFMA.
+//
+// MXFP4 is the other 4-bit activation format that rotations help: E2M1
+// elements with one power-of-two scale per 32 consecutive values ("Rotations
+// for 4-Bit Activations: QuaRot, SpinQuant, and Friends", sections "The full
+// model in NVFP4, on vLLM" and "When to rotate").  With both operands
+// rotated and quantized this way,
+//   Y[m, n] = sum_j 2^(ea[m, j] + eb[n, j]) * sum_{k in block j} a[m, k] b[n, k],
+// and CDNA4 computes exactly that in hardware: v_mfma_scale_f32_16x16x128_f8f6f4
+// with both formats set to FP4 takes, per lane, 16 packed bytes (32 E2M1
+// codes, even k in the low nibble, as the quantizer packs them) and one
+// biased exponent byte for the 32 values it holds, and accumulates in fp32.
+// No widening, no zero-points and no dequantization epilogue are needed.
+//
+// Lane layout of one 16x16x128 product (lane l = 16 g + r): A row r and
+// B row r, K elements 32 g .. 32 g + 31 (packed bytes 16 g .. 16 g + 15 of
+// the 64-byte step), exponent of (row r, block g); C rows 4 g .. 4 g + 3 of
+// column r.  The packed operands keep the INT4 kernels' tiling: A rows
+// straight from global memory into registers, B rows staged through LDS.
+//
+// Exponent bytes: a row holds 4 per 128-wide K step, [4 kt + g].  A lane
+// loads the 16 bytes of four steps of its row at once and gathers the 4
+// bytes of its block g (one per step) into one dword; the MFMA's op_sel
+// then picks byte s of that dword at step s of the group, so no per-step
+// instruction touches the exponents.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+#include "tile.h"
+
+namespace w4a4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBN = 128;       // output columns per workgroup
+constexpr int kKS = 128;       // K elements per step (64 packed bytes of a row)
+constexpr int kRow = 64;       // LDS bytes of one B row per step
+
+// LDS position of 16-byte chunk c (0..3) of B row `row` in a step buffer.
+// The chunk index is XORed with bits 2-3 of the row, so the fragment read
+// (16 consecutive rows, one chunk per lane group) covers 16 distinct 16-byte
+// bank groups within every 16 lanes.
+__device__ __forceinline__ int mx_chunk(int row, int c) { return row * kRow + ((c ^ ((row >> 2) & 3)) << 4); }
+
+// One 16x16x128 FP4 x FP4 product with per-lane E8M0 scales; SEL picks the
+// scale byte inside the scale dwords.
+template <int SEL>
+__device__ __forceinline__ v4f mfma_mx(const uint4& a, uint32_t sa, const uint4& b, uint32_t sb, const v4f& c) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL, (int)sa, SEL, (int)sb);
+}
+
+// 4x4 byte transpose: byte g of d[s] -> byte s of e[g].
+__device__ __forceinline__ uint4 transpose_bytes4(const uint4& d) {
+  const uint32_t t0 = __builtin_amdgcn_perm(d.y, d.x, 0x05010400u);   // d0.0 d1.0 d0.1 d1.1
+  const uint32_t t1 = __builtin_amdgcn_perm(d.y, d.x, 0x07030602u);   // d0.2 d1.2 d0.3 d1.3
+  const uint32_t t2 = __builtin_amdgcn_perm(d.w, d.z, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(d.w, d.z, 0x07030602u);
+  return make_uint4(__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                    __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u));
+}
+
+// Byte g of each of d.x .. d.w gathered into one dword (sel = g | (g + 4) << 8
+// | 0x0C0C0000: bytes g of the low and high source, then two zero bytes).
+__device__ __forceinline__ uint32_t gather_bytes(const uint4& d, uint32_t sel) {
+  const uint32_t lo = __builtin_amdgcn_perm(d.y, d.x, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(d.w, d.z, sel);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- prefill kernel
+// BM x 128 output tile per workgroup, NW waves stacked along M, each wave
+// 16*TM rows x 128 columns (TM x 8 products of 16x16 per step).  Steps are
+// walked in groups of four (the four bytes of an exponent dword); A is
+// loaded two steps ahead into registers, B two steps ahead into registers
+// and one step ahead into a double-buffered LDS stage, and the exponents of
+// B (shared by every wave) one group ahead into a double-buffered LDS table.
+// A step past the end of K is loaded (harmlessly, inside or past the
+// operand's range) but not multiplied.
+template <int NW, int TM, int WPE>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
+  constexpr int BMD = NW * 16 * TM;
+  constexpr int NT = NW * 64;
+  static_assert(NT <= 512 && 512 % NT == 0, "B staging needs 512 / NT chunks per thread");
+  constexpr int NCB = 512 / NT;          // 16-byte B chunks per thread and step (128 rows x 4)
+  constexpr int BSTAGE = 128 * kRow;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t bexp[2][128 * 4];   // [group parity][B row][block g]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tiles_n = (p.N + kBN - 1) / kBN;
+  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BMD, n0 = tn * kBN;
+  const int nkt = p.K / kKS;
+  const int ngr = (nkt + 3) / 4;
+  const int64_t ldc = p.K / 2, lde = p.K / 32;
+
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.xq + m0 * ldc, (p.M - m0) * ldc);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(p.wq + n0 * ldc, (p.N - n0) * ldc);
+  const __amdgpu_buffer_rsrc_t rae = rsrc(p.xe + m0 * lde, (p.M - m0) * lde);
+  const __amdgpu_buffer_rsrc_t rbe = rsrc(p.we + n0 * lde, (p.N - n0) * lde);
+
+  const int fr = lane & 15, g = lane >> 4;
+  const int a_off = (wave * 16 * TM + fr) * (int)ldc + 16 * g;   // + 16 i ldc + 64 kt
+  const int ae_off = (wave * 16 * TM + fr) * (int)lde;           // + 16 i lde + 16 u
+  const uint32_t gsel = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0C0C0000u;
+  int b_off[NCB], b_lds[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = tid + NT * j;
+    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
+    b_lds[j] = mx_chunk(cb >> 2, cb & 3);
+  }
+  const int bf = mx_chunk(fr, g);        // fragment of column block j at bf + j * 16 * kRow
+  const bool be_stager = tid < 128;      // thread t stages the exponents of B row t
+
+  uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB], ae_raw[TM], be_raw;
+  uint32_t ae[TM], be[8];
+
+  auto load_a = [&](uint4* pa, int kt) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
+  };
+  auto load_b = [&](uint4* pb, int kt) {
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4* pb, int stage) {
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) *reinterpret_cast<uint4*>(smem + stage * BSTAGE + b_lds[j]) = pb[j];
+  };
+  auto load_exps = [&](int u) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      ae_raw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rae, ae_off + i * 16 * (int)lde + 16 * u, 0, 0));
+    if (be_stager)
+      be_raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbe, tid * (int)lde + 16 * u, 0, 0));
+  };
+  auto store_bexp = [&](int par) {
+    if (be_stager) *reinterpret_cast<uint4*>(&bexp[par][4 * tid]) = transpose_bytes4(be_raw);
+  };
+  auto take_exps = [&](int par) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ae[i] = gather_bytes(ae_raw[i], gsel);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) be[j] = bexp[par][4 * (16 * j + fr) + g];
+  };
+
+  v4f acc[TM][8];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](auto sel, const uint4* pa, int stage) {
+    constexpr int S = decltype(sel)::value;
+    const uint8_t* Bs = smem + stage * BSTAGE;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 b = *reinterpret_cast<const uint4*>(Bs + j * 16 * kRow + bf);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i][j] = mfma_mx<S>(pa[i], ae[i], b, be[j], acc[i][j]);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+
+  // prologue: exponents of group 0, A and B steps 0 and 1 in flight, B step 0
+  // and the B exponents of group 0 in LDS
+  load_exps(0);
+  load_a(pa0, 0);
+  load_b(pb0, 0);
+  load_a(pa1, 1);
+  load_b(pb1, 1);
+  store_bexp(0);
+  store_b(pb0, 0);
+  __syncthreads();
+  for (int u = 0; u < ngr; ++u) {
+    const int kt = 4 * u;
+    const int par = u & 1;
+    take_exps(par);                   // this group's exponents into registers ...
+    load_exps(u + 1);                 // ... and the next group's on their way
+    load_b(pb0, kt + 2);
+    compute(S0{}, pa0, 0);            // step kt (always < nkt)
+    load_a(pa0, kt + 2);
+    store_b(pb1, 1);                  // B step kt+1
+    __syncthreads();
+    load_b(pb1, kt + 3);
+    if (kt + 1 < nkt) compute(S1{}, pa1, 1);
+    load_a(pa1, kt + 3);
+    store_b(pb0, 0);                  // B step kt+2
+    store_bexp(par ^ 1);              // B exponents of group u+1 (the other table was last read in group u-1)
+    __syncthreads();
+    load_b(pb0, kt + 4);
+    if (kt + 2 < nkt) compute(S2{}, pa0, 0);
+    load_a(pa0, kt + 4);
+    store_b(pb1, 1);                  // B step kt+3
+    __syncthreads();
+    load_b(pb1, kt + 5);
+    if (kt + 3 < nkt) compute(S3{}, pa1, 1);
+    load_a(pa1, kt + 5);
+    store_b(pb0, 0);                  // B step kt+4
+    __syncthreads();
+  }
+
+  // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
+  // block; a quad transpose gives each lane 4 consecutive columns of one
+  // row, stored as one 16-byte write.
+  const int k4 = fr & 3;
+  const bool vec_ok = (p.ldy & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = m0 + wave * 16 * TM + 16 * i + 4 * g + k4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      quad_transpose4(y, k4);
+      const int64_t c0 = n0 + 16 * j + (fr & ~3);     // this lane now holds row `row`, columns c0..c0+3
+      if (row < p.M) {
+        float* dst = p.y + row * p.ldy + c0;
+        if (vec_ok && c0 + 3 < p.N) {
+          store_stream4(dst, y);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (c0 + c < p.N) dst[c] = y[c];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode kernel (M <= 16)
+// The product is weight-bandwidth bound: one workgroup per 16 output
+// columns, its 4 waves splitting the K steps (wave w takes steps w, w+4, ...)
+// with 8 steps of loads in flight, partial sums added through LDS.  Rows of
+// X beyond M and steps beyond K read as zero codes through the buffer range
+// checks (a zero code times any scale is zero).
+__global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
+  __shared__ v4f red[3][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int nkt = p.K / kKS;
+  const int ldc = p.K / 2, lde = p.K / 32;
+  const int64_t nw = p.N - n0 < 16 ? p.N - n0 : 16;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, p.M * ldc);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(p.wq + n0 * ldc, nw * ldc);
+  const __amdgpu_buffer_rsrc_t rxe = rsrc(p.xe, p.M * lde);
+  const __amdgpu_buffer_rsrc_t rwe = rsrc(p.we + n0 * lde, nw * lde);
+  const int c_off = r * ldc + 16 * g;
+  const int e_off = r * lde + g;
+
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t0 = 0; 4 * t0 < nkt; t0 += 8) {
+    uint4 xa[8], wb[8];
+    uint32_t xe[8], we[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kt = wave + 4 * (t0 + u);
+      const bool ok = kt < nkt;
+      const int co = ok ? c_off + kt * 64 : 0x7FFFFFF0;
+      const int eo = ok ? e_off + kt * 4 : 0x7FFFFFF0;
+      wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, co, 0, 0));
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, co, 0, 0));
+      we[u] = __builtin_amdgcn_raw_buffer_load_b8(rwe, eo, 0, 0);
+      xe[u] = __builtin_amdgcn_raw_buffer_load_b8(rxe, eo, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = mfma_mx<0>(xa[u], xe[u], wb[u], we[u], acc);
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    acc += red[0][lane];
+    acc += red[1][lane];
+    acc += red[2][lane];
+    const int64_t col = n0 + r;
+    if (col < p.N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 4 * g + v;
+        if (row < p.M) p.y[row * p.ldy + col] = acc[v];
+      }
+    }
+  }
+}
+
+hipError_t launch_mx_gemm(const MxGemmParams& p, hipStream_t st) {
+  if (p.M == 0) return hipSuccess;
+  if (p.M <= 16) {
+    const int64_t grid = (p.N + 15) / 16;
+    W4A4_LAUNCH(mx_gemm_decode_kernel, dim3((uint32_t)grid), dim3(256), 0, st, p);
+  } else if (p.M > 512) {
+    const int64_t grid = ((p.M + 255) / 256) * ((p.N + kBN - 1) / kBN);
+    W4A4_LAUNCH((mx_gemm_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+  } else {
+    const int64_t grid = ((p.M + 63) / 64) * ((p.N + kBN - 1) / kBN);
+    W4A4_LAUNCH((mx_gemm_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4a4

@@ -277,6 +277,48 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
         const int gs = quad_sum((int)(gsb - 32u * (kRneMagicBits + 8u)));
         if (valid && q == 0) p.gsum[row * p.nb + blk] = gs;
       }
+    } else if constexpr (MODE == kModeMx) {
+      // ---- MXFP4: blocks of 32 (elements 32 r4 .. 32 r4 + 31 of this 128-block,
+      // 8 in each lane of the quad), y = fl32(z / sqrt(b)), a power-of-two
+      // scale 2^e with e = floor(log2 max|y|) - 2 (stored biased, e + 127,
+      // at least 0), E2M1 codes rounded to nearest with ties to the even code
+      // and saturation at 6
+      const float sr = sgn * p.cdiv;     // (sgn z) * (sgn r) = z * r, one rounding
+      uint32_t sbytes = 0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float y[8];
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = v[8 * r4 + e] * sr;
+          am = fmaxf(am, fabsf(y[e]));
+        }
+        am = quad_max(am);
+        const uint32_t ex = (fbits(am) >> 23) & 0xFFu;
+        const uint32_t byte = ex > 2u ? ex - 2u : 0u;        // e + 127, clamped at e = -127
+        const float inv = bitsf((254u - byte) << 23);          // 2^-e (exact scaling)
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = y[e] * inv;
+          const float a = fabsf(t);
+          uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+          c |= (t < 0.0f && c != 0u) ? 8u : 0u;
+          w |= c << (4 * e);
+        }
+        words[r4] = w;
+        sbytes |= byte << (8 * r4);
+      }
+      if (valid) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<uint32_t*>(p.codes + crow + blk * 64 + 16 * r4 + 4 * q) = words[r4];
+        if (q == 0)
+          *reinterpret_cast<uint32_t*>(p.mx_scales + row * (int64_t)(p.K / 32) + blk * 4) = sbytes;
+      }
     } else {
       // ---- asymmetric, one group per 128-block
       float mn = 0.0f, mx = 0.0f;
@@ -332,17 +374,17 @@ hipError_t launch_t(const RQParams& p, int threads, size_t lds, int64_t grid, hi
   return hipGetLastError();
 }
 
-template <bool GSUM>
+template <int MODE, bool GSUM>
 hipError_t launch_full(const RQParams& p, int logf, int threads, size_t lds, int64_t grid,
                        hipStream_t st) {
   switch (logf) {
-    case 1: return launch_t<kModeSym, 1, GSUM, false>(p, threads, lds, grid, st);
-    case 2: return launch_t<kModeSym, 2, GSUM, false>(p, threads, lds, grid, st);
-    case 3: return launch_t<kModeSym, 3, GSUM, false>(p, threads, lds, grid, st);
-    case 4: return launch_t<kModeSym, 4, GSUM, false>(p, threads, lds, grid, st);
-    case 5: return launch_t<kModeSym, 5, GSUM, false>(p, threads, lds, grid, st);
-    case 6: return launch_t<kModeSym, 6, GSUM, false>(p, threads, lds, grid, st);
-    case 7: return launch_t<kModeSym, 7, GSUM, false>(p, threads, lds, grid, st);
+    case 1: return launch_t<MODE, 1, GSUM, false>(p, threads, lds, grid, st);
+    case 2: return launch_t<MODE, 2, GSUM, false>(p, threads, lds, grid, st);
+    case 3: return launch_t<MODE, 3, GSUM, false>(p, threads, lds, grid, st);
+    case 4: return launch_t<MODE, 4, GSUM, false>(p, threads, lds, grid, st);
+    case 5: return launch_t<MODE, 5, GSUM, false>(p, threads, lds, grid, st);
+    case 6: return launch_t<MODE, 6, GSUM, false>(p, threads, lds, grid, st);
+    case 7: return launch_t<MODE, 7, GSUM, false>(p, threads, lds, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -387,10 +429,15 @@ hipError_t launch_rotate_quant(RQParams p, int mode, bool full, bool gsum, bool 
   if (logf > 0) lds = (size_t)g.rows_per_wg * p.K * sizeof(float);
   else if (mode == kModeSym && g.seg > kWave) lds = (size_t)g.rows_per_wg * 16 * sizeof(float);
   if (g.grid == 0) return hipSuccess;
+  if (mode == kModeMx) {
+    if (strided || gsum) return hipErrorInvalidValue;
+    if (logf > 0) return launch_full<kModeMx, false>(p, logf, g.threads, lds, g.grid, st);
+    return launch_t<kModeMx, 0, false, false>(p, g.threads, lds, g.grid, st);
+  }
   if (mode == kModeSym) {
     if (strided) return hipErrorInvalidValue;
-    if (logf > 0) return gsum ? launch_full<true>(p, logf, g.threads, lds, g.grid, st)
-                              : launch_full<false>(p, logf, g.threads, lds, g.grid, st);
+    if (logf > 0) return gsum ? launch_full<kModeSym, true>(p, logf, g.threads, lds, g.grid, st)
+                              : launch_full<kModeSym, false>(p, logf, g.threads, lds, g.grid, st);
     return gsum ? launch_t<kModeSym, 0, true, false>(p, g.threads, lds, g.grid, st)
                 : launch_t<kModeSym, 0, false, false>(p, g.threads, lds, g.grid, st);
   }

@@ -94,3 +94,55 @@ def rel_fro(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ---------------------------------------------------------------- MXFP4
+E2M1_TIES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def near_mx_tie(t: np.ndarray) -> np.ndarray:
+    """|t| within TIE_WINDOW (relative to the tie, at least absolute) of a
+    midpoint between two E2M1 magnitudes."""
+    a = np.abs(np.asarray(t, np.float64))
+    d = np.abs(a[..., None] - E2M1_TIES)
+    return (d < TIE_WINDOW * np.maximum(1.0, E2M1_TIES)).any(axis=-1)
+
+
+def check_mx(packed_gpu, sbytes_gpu, ref: dict, exact: bool = False) -> dict:
+    """Compare GPU MXFP4 codes / scale bytes with oracle `rotate_mx_quant` output.
+
+    An exponent may differ (by one) only where the oracle's block maximum is
+    within TIE_WINDOW of a power of two; codes are then checked against the
+    oracle's rounding under the GPU's exponent, and may differ (by one
+    magnitude step) only near an E2M1 midpoint."""
+    y = np.asarray(ref["y32"], np.float64)
+    R, K = y.shape
+    J = K // 32
+    e_ref = np.asarray(ref["scale_e"], np.int64)
+    e_gpu = np.asarray(sbytes_gpu, np.int64).reshape(R, J) - 127
+    ediff = e_gpu != e_ref
+    if exact:
+        assert not ediff.any(), f"{int(ediff.sum())} exponent mismatches on exact inputs"
+    else:
+        amax = np.abs(y.reshape(R, J, 32)).max(axis=-1)
+        pos = amax > 0
+        mant = np.where(pos, amax / np.exp2(np.floor(np.log2(np.where(pos, amax, 1.0)))), 1.5)
+        near_p2 = (np.abs(mant - 1.0) < TIE_WINDOW) | (np.abs(mant - 2.0) < TIE_WINDOW)
+        assert np.all(near_p2[ediff]), "an exponent differs away from a power of two"
+        assert np.all(np.abs(e_gpu - e_ref)[ediff] == 1)
+    t = y.reshape(R, J, 32) / np.exp2(e_gpu.astype(np.float64))[..., None]
+    c_exp = O.e2m1_round(t).reshape(R, K)
+    c_gpu = O.unpack_nibbles(packed_gpu, signed=False).reshape(R, K)
+    diff = c_gpu != c_exp
+    n_flip = int(diff.sum())
+    if exact:
+        assert n_flip == 0, f"{n_flip} code mismatches on exact inputs"
+    else:
+        mg, me = c_gpu & 7, c_exp & 7
+        assert np.all(np.abs(mg - me)[diff] == 1), "a code differs by more than one step"
+        same_sign = ((c_gpu ^ c_exp) & 8) == 0
+        assert np.all((same_sign | (mg == 0) | (me == 0))[diff]), "a code differs in sign"
+        assert np.all(near_mx_tie(t.reshape(R, K)[diff])), "a code differs away from a midpoint"
+        assert n_flip <= MAX_FLIP_FRAC * c_exp.size, f"{n_flip} flips in {c_exp.size}"
+    _check_bytes(np.asarray(packed_gpu).reshape(R, -1), c_exp, diff)
+    return dict(flips=n_flip, scale_flips=int(ediff.sum()), elements=c_exp.size)

@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-              "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode"):
+              "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode",
+              "rotate_quant_mxfp4", "mxfp4_gemm"):
         assert n in names
 
 
@@ -28,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for n in _declared():
         assert hasattr(lib, n), n
-    assert lib.w4a4_abi_version() == 2
+    assert lib.w4a4_abi_version() == 3
     src = open(HEADER).read()
     assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
 
@@ -143,6 +144,46 @@ def test_kv_validation(args, status):
 ])
 def test_kv4_attention_validation(args, status):
     assert _lib.call("kv4_attention_decode", *args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # x, M, K, ldx, had_block, signs, codes, scales, stream
+    ((NUL, 4, 128, 128, 128, NUL, A, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, NUL, NUL, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 128, 128, 128, NUL, A, NUL, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 160, 160, 128, NUL, A, A, NUL), _lib.W4A4_ERR_SHAPE),          # K % 128
+    ((A, 4, 384, 384, 0, NUL, A, A, NUL), _lib.W4A4_ERR_SHAPE),            # full needs 2^p
+    ((A, 4, 256, 128, 128, NUL, A, A, NUL), _lib.W4A4_ERR_SHAPE),          # ldx < K
+    ((A, -1, 128, 128, 128, NUL, A, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, 4, 128, 128, 32, NUL, A, A, NUL), _lib.W4A4_ERR_MODE),            # had_block
+    ((A, 4, 128, 128, 128, NUL, A, A + 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 4, 128, 128, 128, A + 2, A, A, NUL), _lib.W4A4_ERR_ALIGN),        # signs alignment
+    ((A, 4, 128, 132, 128, NUL, A, A, NUL), _lib.W4A4_ERR_ALIGN),          # ldx % 8
+    ((NUL, 0, 128, 128, 128, NUL, NUL, NUL, NUL), _lib.W4A4_OK),           # M == 0: no-op
+])
+def test_rotate_quant_mxfp4_validation(args, status):
+    assert _lib.call("rotate_quant_mxfp4", *args) == status
+    assert (_lib.last_error() == "") == (status == _lib.W4A4_OK)
+
+
+@pytest.mark.parametrize("args,status", [
+    # xc, xe, wc, we, M, N, K, y, ldy, stream
+    ((NUL, A, A, A, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, NUL, A, A, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, NUL, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, 4, 4, 128, NUL, 4, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, 4, 0, 128, A, 4, NUL), _lib.W4A4_ERR_SHAPE),            # N == 0
+    ((A, A, A, A, 4, 4, 96, A, 4, NUL), _lib.W4A4_ERR_SHAPE),             # K % 128
+    ((A, A, A, A, 4, 4, 262144, A, 4, NUL), _lib.W4A4_ERR_SHAPE),         # K too large
+    ((A, A, A, A, 4, 4, 128, A, 3, NUL), _lib.W4A4_ERR_SHAPE),            # ldy < N
+    ((A, A, A, A, -2, 4, 128, A, 4, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A + 4, A, A, 4, 4, 128, A, 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, A, A, A, 4, 4, 128, A + 8, 4, NUL), _lib.W4A4_ERR_ALIGN),
+    ((NUL, NUL, NUL, NUL, 0, 4, 128, NUL, 4, NUL), _lib.W4A4_OK),         # M == 0: no-op
+])
+def test_mxfp4_gemm_validation(args, status):
+    assert _lib.call("mxfp4_gemm", *args) == status
+    assert (_lib.last_error() == "") == (status == _lib.W4A4_OK)
 
 
 def test_time_next_launch_arming():

@@ -162,3 +162,10 @@ def hadamard_signs(n: int, seed: int = 0) -> np.ndarray:
     signs do is the method's business, not this module's."""
     rng = np.random.default_rng(np.random.SeedSequence(66_000 + seed))
     return np.where(rng.integers(0, 2, size=n) == 0, 1.0, -1.0).astype(np.float16)
+
+
+def random_bytes(seed: int, rows: int, cols: int, lo: int = 0, hi: int = 255) -> np.ndarray:
+    """rows x cols uint8 drawn uniformly from [lo, hi]: raw operand bytes
+    (packed 4-bit codes, biased exponents) for tests of the products alone."""
+    rng = np.random.default_rng(np.random.SeedSequence(88_000 + seed))
+    return rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.uint8)
