@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+FP4_PEAK_TOPS = 10100.0        # MI355X dense fp4 MFMA (MXFP4 products), TFLOP/s
 NSETS = 8
 
 
@@ -128,7 +129,7 @@ def run_suite(torch, R, WL):
     def flush():
         scratch.amax()
 
-    def emit(kernel, config, t, nbytes=None, ops=None):
+    def emit(kernel, config, t, nbytes=None, ops=None, peak=("int8", INT8_PEAK_TOPS)):
         rec = dict(kernel=kernel, config=config, **{k: round(v, 5) for k, v in t.items()})
         if nbytes is not None:
             gbs = nbytes / (t["cold_ms_median"] * 1e-3) / 1e9
@@ -138,7 +139,7 @@ def run_suite(torch, R, WL):
         if ops is not None:
             tops = ops / (t["cold_ms_median"] * 1e-3) / 1e12
             rec.update(ops=ops, bound="mfma", cold_TOPS=round(tops, 1),
-                       cold_frac_int8=round(tops / INT8_PEAK_TOPS, 4),
+                       **{f"cold_frac_{peak[0]}": round(tops / peak[1], 4)},
                        warm_TOPS=round(ops / (t["warm_ms"] * 1e-3) / 1e12, 1))
         print(json.dumps(rec), flush=True)
 
@@ -147,6 +148,11 @@ def run_suite(torch, R, WL):
 
     def act_bytes(M, K, asym=False):
         return 2 * M * K + M * K // 2 + (5 * M * (K // 128) if asym else 4 * M)
+
+    def mx_bytes(M, K):
+        return 2 * M * K + M * K // 2 + M * K // 32
+
+    FP4 = ("fp4", FP4_PEAK_TOPS)
 
     # q_proj family M x 4096 x 4096 (both Hadamard widths), decode rows, down_proj, gate/up
     wq = T(WL.qproj_weight())
@@ -168,7 +174,23 @@ def run_suite(torch, R, WL):
                  _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y), flush),
                  nbytes=(M * 2048 + 4 * M + 4096 * 2048 + 4 * 4096 + 4 * M * 4096) if M <= 16 else None,
                  ops=2 * M * 4096 * 4096)
-    del wq
+    # MXFP4 on the same shapes (128-wide blocks)
+    wmc, wme = R.rotate_quant_mxfp4(wq, 128)
+    emit("rotate_quant_mxfp4", "qproj W 4096x4096 had128",
+         _time_kernel(torch, lambda: R.rotate_quant_mxfp4(wq, 128), flush), nbytes=mx_bytes(4096, 4096))
+    for M in (1, 16, 256, 2048, 8192):
+        x = T(WL.qproj(M=min(M, 2048), with_w=False)["X"])
+        if M > 2048:
+            x = x.repeat(M // 2048, 1)
+        xmc, xme = R.rotate_quant_mxfp4(x, 128)
+        emit("rotate_quant_mxfp4", f"qproj X {M}x4096 had128",
+             _time_kernel(torch, lambda: R.rotate_quant_mxfp4(x, 128), flush), nbytes=mx_bytes(M, 4096))
+        y = torch.empty((M, 4096), dtype=torch.float32, device=dev)
+        emit("mxfp4_gemm", f"{M}x4096x4096 had128",
+             _time_kernel(torch, lambda: R.mxfp4_gemm(xmc, xme, wmc, wme, out=y), flush),
+             nbytes=(M * 2048 + M * 128 + 4096 * 2048 + 4096 * 128 + 4 * M * 4096) if M <= 16 else None,
+             ops=2 * M * 4096 * 4096, peak=FP4)
+    del wq, wmc
     d = WL.downproj()
     x, w = T(d["X"]), T(d["W"])
     del d
@@ -183,7 +205,14 @@ def run_suite(torch, R, WL):
     emit("w4a4_gemm", "downproj 4096x4096x14336",
          _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y), flush),
          ops=2 * 4096 * 4096 * 14336)
-    del x, w, xc, wc, y
+    xmc, xme = R.rotate_quant_mxfp4(x, 128)
+    wmc, wme = R.rotate_quant_mxfp4(w, 128)
+    emit("rotate_quant_mxfp4", "downproj X 4096x14336 had128",
+         _time_kernel(torch, lambda: R.rotate_quant_mxfp4(x, 128), flush), nbytes=mx_bytes(4096, 14336))
+    emit("mxfp4_gemm", "downproj 4096x4096x14336",
+         _time_kernel(torch, lambda: R.mxfp4_gemm(xmc, xme, wmc, wme, out=y), flush),
+         ops=2 * 4096 * 4096 * 14336, peak=FP4)
+    del x, w, xc, wc, y, xmc, wmc
     d = WL.gateup()
     x, w = T(d["X"]), T(d["W"])
     del d
@@ -200,7 +229,13 @@ def run_suite(torch, R, WL):
          _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, xz, wc, ws, act_mode="asym", out=y), flush, n=10,
                       warm_n=10),
          ops=2 * 8192 * 28672 * 8192)
-    del x, w, xc, wc, y
+    del xc, wc
+    xmc, xme = R.rotate_quant_mxfp4(x, 128)
+    wmc, wme = R.rotate_quant_mxfp4(w, 128)
+    emit("mxfp4_gemm", "gateup 8192x28672x8192",
+         _time_kernel(torch, lambda: R.mxfp4_gemm(xmc, xme, wmc, wme, out=y), flush, n=10, warm_n=10),
+         ops=2 * 8192 * 28672 * 8192, peak=FP4)
+    del x, w, y, xmc, wmc
     kv = T(WL.kv()["KV"])
     emit("kv_rotate_quant4", "kv 8x32x4096x128",
          _time_kernel(torch, lambda: R.kv_rotate_quant4(kv), flush),
@@ -244,6 +279,15 @@ def run_only(torch, R, WL, which, steps, had):
               "decode": lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y),
               "act": lambda: R.rotate_quant_act(x, block),
               "weight": lambda: R.quant_weight_offline(w, block)}[which]
+    elif which in ("mx", "mxact", "mxdecode"):
+        d = WL.qproj() if which != "mxdecode" else WL.decode(16)
+        x, w = T(d["X"]), T(d["W"])
+        wc, we = R.rotate_quant_mxfp4(w, 128)
+        xc, xe = R.rotate_quant_mxfp4(x, 128)
+        y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.float32, device=dev)
+        fn = {"mx": lambda: R.mxfp4_gemm(xc, xe, wc, we, out=y),
+              "mxdecode": lambda: R.mxfp4_gemm(xc, xe, wc, we, out=y),
+              "mxact": lambda: R.rotate_quant_mxfp4(x, 128)}[which]
     elif which == "downproj":
         d = WL.downproj()
         x, w = T(d["X"]), T(d["W"])
@@ -284,7 +328,8 @@ def main() -> int:
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
-    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "decode", "gateup", "downproj", "copy"],
+    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "decode", "gateup", "downproj", "copy",
+                                       "mx", "mxact", "mxdecode"],
                     help="launch one kernel --steps times back to back (for rocprofv3 runs)")
     args = ap.parse_args()
 

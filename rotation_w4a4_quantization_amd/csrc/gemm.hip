@@ -508,12 +508,13 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     return hipGetLastError();
   }
   if (mode == kModeSym) {
-    // A-direct kernel.  Large M: 256-row tiles of 8 waves (32 x 128 each) when
-    // there are at least two tiles per CU (two workgroups share a CU), else
-    // 256-row tiles of 16 waves (16 x 128 each) so that one workgroup per CU
-    // still has four waves per SIMD.  M <= 512: 64-row tiles of 4 waves.
-    if (p.M > 512) {
-      const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
+    // A-direct kernel.  256-row tiles of 8 waves (32 x 128 each) when there
+    // are at least two tiles per CU (two workgroups share a CU), else 256-row
+    // tiles of 16 waves (16 x 128 each) so that one workgroup per CU still
+    // has four waves per SIMD; fewer than one 256-row tile per CU: 64-row
+    // tiles of 4 waves (M = 600: 320 workgroups instead of 96).
+    const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
+    if (grid >= 256) {
       if (grid >= 512)
         W4A4_LAUNCH((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
       else
