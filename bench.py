@@ -441,7 +441,7 @@ def main() -> int:
     act_gbs = act_bytes / (kt["rotate_quant_act"] * 1e-3) / 1e9
     w_gbs = w_bytes / (kt["quant_weight_offline"] * 1e-3) / 1e9
 
-    traffic = profile_traffic(f"w4a4_gemm_qproj_had{args.had}", src_hash("gemm.hip", "common.h"))
+    traffic = profile_traffic(f"w4a4_gemm_qproj_had{args.had}", src_hash("gemm.hip", "common.h", "tile.h"))
     out = {
         "metric": "W4A4 GEMM TOPS (frac INT8 MFMA peak) + rotate+quant GB/s, M×4096×4096",
         "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
