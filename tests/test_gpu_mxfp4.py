@@ -87,6 +87,39 @@ def test_rotate_quant_mxfp4_exact_class(K, block):
     check_mx(c, e, O.rotate_mx_quant(x, block), exact=True)
 
 
+def test_rotate_quant_mxfp4_exact_midpoints():
+    """Rows x = H c (c sparse: in every 32-block one +-5, which fixes the block
+    maximum, and three draws from the E2M1 midpoints).  With the full-width
+    K = 1024 transform, z = H x = K c exactly, y = z / 32 = 32 c, e = 5 and
+    y / 2^e = c: every non-zero element lies exactly on a midpoint, on both
+    sides, so the codes pin the ties-to-even rule (and saturation-free
+    rounding up to 5) bit for bit."""
+    K, rows = 1024, 64
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    pos = WL.random_bytes(31, rows, 3 * (K // 32), 0, 31).astype(np.int64)
+    val = WL.random_bytes(32, rows, 3 * (K // 32), 0, 13).astype(np.int64)
+    c = np.zeros((rows, K))
+    for r in range(rows):
+        for j in range(K // 32):
+            c[r, 32 * j + (r + j) % 32] = 5.0 if (r + j) % 2 else -5.0
+            for u in range(3):
+                p_ = 32 * j + (((r + j) % 32) + 1 + pos[r, 3 * j + u] % 31) % 32
+                v_ = mids[val[r, 3 * j + u] % 7] * (1.0 if val[r, 3 * j + u] < 7 else -1.0)
+                c[r, p_] = v_
+    x64 = O.rotate(c, K)                       # H c (the unnormalized transform)
+    x = x64.astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), x64), "H c must be exact in fp16"
+    ref = O.rotate_mx_quant(x, K)
+    assert np.all(ref["scale_e"] == 5)
+    t = ref["y32"].astype(np.float64) / 32.0
+    assert np.array_equal(t, c)
+    n_ties = int(np.isin(np.abs(t), mids).sum())
+    assert n_ties >= 3 * rows * (K // 32)
+    cg, eg = gpu_mx(x, "full")
+    st = check_mx(cg, eg, ref, exact=True)
+    print("exact midpoints", n_ties, st)
+
+
 @pytest.mark.parametrize("block", [128, "full"])
 def test_rotate_quant_mxfp4_signs(block):
     K = 2048
