@@ -174,6 +174,15 @@ def run_suite(torch, R, WL):
                  _time_kernel(torch, lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y), flush),
                  nbytes=(M * 2048 + 4 * M + 4096 * 2048 + 4 * 4096 + 4 * M * 4096) if M <= 16 else None,
                  ops=2 * M * 4096 * 4096)
+    # decode linear in one launch (activation rotate+quant fused into the decode GEMM);
+    # compare with the rotate_quant_act + w4a4_gemm lines above
+    wc, ws, _ = R.quant_weight_offline(wq, 128)
+    for M in (1, 4, 16):
+        x = T(WL.decode(M, with_w=False)["X"])
+        y = torch.empty((M, 4096), dtype=torch.float32, device=dev)
+        emit("w4a4_decode_fused", f"{M}x4096x4096 had128",
+             _time_kernel(torch, lambda: R.w4a4_decode_fused(x, wc, ws, out=y), flush),
+             nbytes=2 * M * 4096 + 4096 * 2048 + 4 * 4096 + 4 * M * 4096, ops=2 * M * 4096 * 4096)
     # MXFP4 on the same shapes (128-wide blocks)
     wmc, wme = R.rotate_quant_mxfp4(wq, 128)
     emit("rotate_quant_mxfp4", "qproj W 4096x4096 had128",
@@ -279,6 +288,12 @@ def run_only(torch, R, WL, which, steps, had):
               "decode": lambda: R.w4a4_gemm(xc, xs, None, wc, ws, out=y),
               "act": lambda: R.rotate_quant_act(x, block),
               "weight": lambda: R.quant_weight_offline(w, block)}[which]
+    elif which == "fused":
+        d = WL.decode(16)
+        x, w = T(d["X"]), T(d["W"])
+        wc, ws, _ = R.quant_weight_offline(w, 128)
+        y = torch.empty((16, w.shape[0]), dtype=torch.float32, device=dev)
+        fn = lambda: R.w4a4_decode_fused(x, wc, ws, out=y)                    # noqa: E731
     elif which in ("mx", "mxact", "mxdecode"):
         d = WL.qproj() if which != "mxdecode" else WL.decode(16)
         x, w = T(d["X"]), T(d["W"])
@@ -329,7 +344,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
     ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "decode", "gateup", "downproj", "copy",
-                                       "mx", "mxact", "mxdecode"],
+                                       "mx", "mxact", "mxdecode", "fused"],
                     help="launch one kernel --steps times back to back (for rocprofv3 runs)")
     args = ap.parse_args()
 

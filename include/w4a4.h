@@ -84,10 +84,10 @@ typedef enum {
 enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
 enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
 
-#define W4A4_ABI_VERSION 3
+#define W4A4_ABI_VERSION 4
 
 /*
- * had_signs (the four rotate calls): NULL, or a device array of K fp16
+ * had_signs (the rotate calls and w4a4_decode_fused): NULL, or a device array of K fp16
  * values (D = 128 for kv_rotate_quant4), each +1.0 or -1.0, 16-byte aligned.
  * Non-NULL turns the rotation into the randomized Hadamard Q = diag(d) H / sqrt(b):
  * element k of every row is multiplied by d[k] (its sign bit is flipped
@@ -167,6 +167,29 @@ W4A4_API w4a4_status w4a4_gemm(const uint8_t* x_codes, const float* x_scales, co
                       int32_t act_mode, const uint8_t* w_codes, const float* w_scales,
                       const int32_t* w_gsum, int64_t M, int64_t N, int64_t K,
                       float* y, int64_t ldy, void* stream);
+
+/*
+ * w4a4_decode_fused - the decode linear layer in one launch: exactly
+ * rotate_quant_act(x, M, K, ldx, W4A4_HAD_128, had_signs, W4A4_ACT_SYM_TOKEN)
+ * followed by w4a4_gemm(symmetric) on w_codes / w_scales, with the
+ * activation codes and scales kept on chip.  Y equals the two-call result
+ * bit for bit.
+ *   Page "Rotations for 4-Bit Activations: QuaRot, SpinQuant, and Friends",
+ *   section "Where the rotations go" (the online rotation is fused with the
+ *   quantization; here also with the product), section "A rotation changes
+ *   nothing, and that is the point".
+ *
+ *   x_f16    [M][ldx] fp16; 1 <= M <= 16; K a multiple of 128 in [128, 8192],
+ *            M * K <= 65536; ldx >= K, a multiple of 8, < 2^24.
+ *   had_signs  NULL or the fp16 +-1 vector [K] (as in rotate_quant_act).
+ *   w_codes  [N][K/2], w_scales [N] fp32, as quant_weight_offline writes them
+ *            with had_block 128 and the same had_signs.
+ *   y        [M][ldy] fp32 (written); N >= 1, ldy >= N.
+ *   Larger M or K: use the two calls.
+ */
+W4A4_API w4a4_status w4a4_decode_fused(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
+                             const uint16_t* had_signs, const uint8_t* w_codes, const float* w_scales,
+                             int64_t N, float* y, int64_t ldy, void* stream);
 
 /*
  * kv_rotate_quant4 - KV-cache step: every (b, h, s) head vector of D = 128

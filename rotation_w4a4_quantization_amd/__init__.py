@@ -11,6 +11,7 @@ exception.  Every step of the computation runs in the library's kernels.
     codes, scales, zeros = rotate_quant_act(x, had_block=128, signs=d)
     wq, ws, gsum = quant_weight_offline(w, had_block=128, signs=d)
     y = w4a4_gemm(codes, scales, zeros, wq, ws, act_mode="sym")
+    y = w4a4_decode_fused(x_small, wq, ws)      # M <= 16: both steps in one launch
     kc, ks, kz = kv_rotate_quant4(kv)
     o = kv4_attention_decode(q, kc, ks, kz, vc, vs, vz)   # decode attention on the INT4 cache
     # MXFP4 (E2M1 codes, a power-of-two scale per 32) on the scaled FP4 MFMA
@@ -27,7 +28,8 @@ from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HA
                    last_error)
 
 __all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-           "kv4_attention_decode", "rotate_quant_mxfp4", "mxfp4_gemm", "abi_version", "W4A4Error"]
+           "kv4_attention_decode", "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "abi_version",
+           "W4A4Error"]
 
 _MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
 
@@ -264,4 +266,30 @@ def mxfp4_gemm(x_codes, x_scales, w_codes, w_scales, out: torch.Tensor | None = 
     st = _lib.call("mxfp4_gemm", _ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales), M, N, K,
                    _ptr(y), y.stride(0), _stream(dev))
     _check(st, "mxfp4_gemm")
+    return y
+
+
+def w4a4_decode_fused(x: torch.Tensor, w_codes, w_scales, signs=None, out: torch.Tensor | None = None):
+    """Y fp32 [M, N] = w4a4_gemm(rotate_quant_act(x, 128, "sym"), W) for M <= 16
+    rows in one launch (bit-identical to the two calls)."""
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    _need(w_codes, torch.uint8, "w_codes")
+    _need(w_scales, torch.float32, "w_scales")
+    if not w_codes.is_contiguous() or not w_scales.is_contiguous():
+        raise ValueError("w_codes and w_scales must be contiguous")
+    M, K = x.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("x and w_codes disagree on K")
+    dev = x.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(y, torch.float32, "out")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] != N or y.stride(1) != 1:
+        raise ValueError("out must be [M, N] with contiguous rows")
+    sg = _signs(signs, K, dev)
+    st = _lib.call("w4a4_decode_fused", _ptr(x), M, K, x.stride(0), _ptr(sg), _ptr(w_codes), _ptr(w_scales), N,
+                   _ptr(y), y.stride(0), _stream(dev))
+    _check(st, "w4a4_decode_fused")
     return y

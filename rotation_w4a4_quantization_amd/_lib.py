@@ -29,6 +29,7 @@ SIGNATURES = {
     "kv4_attention_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
                              _vp, _vp, _vp],
     "rotate_quant_mxfp4": [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
+    "w4a4_decode_fused": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "mxfp4_gemm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
 }
 

@@ -187,6 +187,42 @@ w4a4_status quant_weight_offline(const uint16_t* w_f16, int64_t N, int64_t K, in
                   "quant_weight_offline");
 }
 
+w4a4_status w4a4_decode_fused(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
+                              const uint16_t* had_signs, const uint8_t* w_codes, const float* w_scales,
+                              int64_t N, float* y, int64_t ldy, void* stream) {
+  TimingScope timing_scope;
+  if (M < 1 || M > 16) return fail(W4A4_ERR_SHAPE, "M=%lld must be in [1, 16]", (long long)M);
+  if (K < 128 || K % 128 != 0 || K > 8192)
+    return fail(W4A4_ERR_SHAPE, "K=%lld must be a multiple of 128 in [128, 8192]", (long long)K);
+  if (M * K > 65536)
+    return fail(W4A4_ERR_SHAPE, "M*K=%lld exceeds 65536 (the codes of all rows live in LDS)", (long long)(M * K));
+  if (ldx < K) return fail(W4A4_ERR_SHAPE, "ldx=%lld must be >= K=%lld", (long long)ldx, (long long)K);
+  if (ldx >= (int64_t(1) << 24)) return fail(W4A4_ERR_SHAPE, "ldx=%lld must be < 2^24 elements", (long long)ldx);
+  if (ldx % 8 != 0) return fail(W4A4_ERR_ALIGN, "ldx=%lld must be a multiple of 8 elements", (long long)ldx);
+  if (N < 1 || N >= (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "N=%lld out of range [1, 2^31)", (long long)N);
+  if (ldy < N) return fail(W4A4_ERR_SHAPE, "ldy=%lld must be >= N=%lld", (long long)ldy, (long long)N);
+  if (!x_f16 || !w_codes || !w_scales || !y)
+    return fail(W4A4_ERR_NULL, "x_f16, w_codes, w_scales and y must be non-NULL");
+  if (!aligned16(x_f16) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) ||
+      (had_signs && !aligned16(had_signs)))
+    return fail(W4A4_ERR_ALIGN, "every pointer must be 16-byte aligned");
+  if (w4a4_status s = check_device()) return s;
+
+  w4a4::FusedDecodeParams p{};
+  p.x = x_f16;
+  p.signs = had_signs;
+  p.wq = w_codes;
+  p.ws = w_scales;
+  p.y = y;
+  p.N = N;
+  p.ldy = ldy;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.ldx = (int32_t)ldx;
+  p.cdiv = sym_cdiv(128);
+  return launched(w4a4::launch_decode_fused(p, (hipStream_t)stream), "w4a4_decode_fused");
+}
+
 w4a4_status rotate_quant_mxfp4(const uint16_t* x_f16, int64_t M, int64_t K, int64_t ldx,
                                int32_t had_block, const uint16_t* had_signs, uint8_t* codes,
                                uint8_t* scales_e8m0, void* stream) {

@@ -23,8 +23,6 @@
 
 namespace w4a4 {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 namespace {
 
 constexpr int BN = 128, BK = 128;   // BK in 4-bit elements
@@ -38,15 +36,6 @@ constexpr int LROW = 128;                      // LDS bytes per int8 row (one K 
 // 16-byte padding or a (row >> 1) swizzle.
 __device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_chunk(int row, int c) { return row * LROW + ((c ^ lds_swz(row)) << 4); }
-
-__device__ __forceinline__ void widen_signed(uint32_t p, uint32_t& even16, uint32_t& odd16) {
-  even16 = (p << 4) & 0xF0F0F0F0u;
-  odd16 = p & 0xF0F0F0F0u;
-}
-
-__device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
 
 }  // namespace
 

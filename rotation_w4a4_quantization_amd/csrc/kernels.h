@@ -54,6 +54,21 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st);
 hipError_t gemm_prepare_device();   // once per device, before the first GEMM launch
 
+// Decode W4A4 linear in one launch: symmetric per-token INT4 of the rotated
+// activation rows (128-blocks) fused into the weight-streaming GEMM.
+struct FusedDecodeParams {
+  const uint16_t* x;      // [M][ldx] fp16
+  const uint16_t* signs;  // optional [K] fp16 +-1
+  const uint8_t* wq;      // [N][K/2]
+  const float* ws;        // [N]
+  float* y;               // [M][ldy]
+  int64_t N, ldy;
+  int32_t M, K, ldx;
+  float cdiv;             // fl32(7 sqrt(128))
+};
+
+hipError_t launch_decode_fused(const FusedDecodeParams& p, hipStream_t st);
+
 // MXFP4 GEMM: Y = sum over 32-blocks of 2^(ea + eb) * (E2M1 codes . E2M1 codes).
 struct MxGemmParams {
   const uint8_t* xq;    // [M][K/2] packed E2M1 codes

@@ -24,6 +24,7 @@
 // of the exact product z * inv) and 8 codes are packed per dword.
 #include "common.h"
 #include "kernels.h"
+#include "rq_block.h"
 
 namespace w4a4 {
 
@@ -96,18 +97,6 @@ __device__ __forceinline__ void fwht_block_axis(float* buf, int lt) {
   }
 }
 
-// Pack 8 codes whose value sits in the low 4 bits of each word (bits 4..7
-// zero, higher bits ignored) into one dword, element 0 in bits 3:0.
-__device__ __forceinline__ uint32_t pack8(const uint32_t* b) {
-  const uint32_t p01 = (b[1] << 4) | b[0];
-  const uint32_t p23 = (b[3] << 4) | b[2];
-  const uint32_t p45 = (b[5] << 4) | b[4];
-  const uint32_t p67 = (b[7] << 4) | b[6];
-  const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);   // [p01.b0, p23.b0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(p67, p45, 0x0C0C0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                   // [lo.b0, lo.b1, hi.b0, hi.b1]
-}
-
 }  // namespace
 
 template <int MODE, int LOG_NB_FULL, bool GSUM, bool STRIDED, bool SIGNS>
@@ -178,33 +167,9 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
       }
     }
 
-    // the first butterfly (element bit 0: the two halves of a dword) is fused
-    // with the conversion to fp32
+    // 128-point transform of the block: afterwards this lane holds sgn * z
     float v[32];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const uint32_t d[4] = {w[r4].x, w[r4].y, w[r4].z, w[r4].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cvt_bfly(d[j], v[8 * r4 + 2 * j], v[8 * r4 + 2 * j + 1]);
-    }
-    // remaining register bits (element bits 1-2, 5-6) ...
-#pragma unroll
-    for (int b = 2; b < 32; b <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (!(i & b)) {
-          const float a = v[i], c = v[i | b];
-          v[i] = a + c;
-          v[i | b] = a - c;
-        }
-      }
-    }
-    // ... and the two quad-lane bits (element bits 3-4): afterwards this lane
-    // holds sgn * z
-    dpp_bfly_q0(v, s0);
-    dpp_bfly_q0(v + 16, s0);
-    dpp_bfly_q1(v, s1);
-    dpp_bfly_q1(v + 16, s1);
+    fwht128_quad(w, v, s0, s1);
 
     // ---- full width: butterflies over the block index through LDS.  Values
     // at one in-block position share their sign, so the signed values
@@ -257,15 +222,7 @@ __global__ void __launch_bounds__(512) rotate_quant_kernel(RQParams p) {
       // in offset-8 binary, turned into two's complement by the final xor.
       uint32_t gsb = 0;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        uint32_t b[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          b[e] = fbits(fmaf(v[8 * r4 + e], sinv, kRneMagic + 8.0f));
-          if constexpr (GSUM) gsb += b[e];
-        }
-        words[r4] = pack8(b) ^ 0x88888888u;
-      }
+      for (int r4 = 0; r4 < 4; ++r4) words[r4] = sym_word(v + 8 * r4, sinv, gsb);
       if (valid) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)

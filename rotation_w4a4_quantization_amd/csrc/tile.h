@@ -1,9 +1,24 @@
-// Output-tile helpers shared by the GEMM kernels (gfx950, wave64).
+// Helpers shared by the GEMM kernels (gfx950, wave64): INT4 -> int8
+// widening, the int8 MFMA, tile order and the output tile epilogue.
 #pragma once
 
 #include "common.h"
 
 namespace w4a4 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Packed two's-complement nibbles -> int8 lanes scaled by 16, without
+// per-element shifts: the bytes of (p << 4) & 0xF0F0F0F0 are 16 x the even
+// nibbles and those of p & 0xF0F0F0F0 16 x the odd ones, sign included.
+__device__ __forceinline__ void widen_signed(uint32_t p, uint32_t& even16, uint32_t& odd16) {
+  even16 = (p << 4) & 0xF0F0F0F0u;
+  odd16 = p & 0xF0F0F0F0u;
+}
+
+__device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
 
 // Tile coordinates of this workgroup.  Tiles are walked in groups of 16 tile
 // rows, column by column inside a group, so the workgroups resident at one

@@ -21,7 +21,7 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
               "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode",
-              "rotate_quant_mxfp4", "mxfp4_gemm"):
+              "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused"):
         assert n in names
 
 
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for n in _declared():
         assert hasattr(lib, n), n
-    assert lib.w4a4_abi_version() == 3
+    assert lib.w4a4_abi_version() == 4
     src = open(HEADER).read()
     assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
 
@@ -183,6 +183,28 @@ def test_rotate_quant_mxfp4_validation(args, status):
 ])
 def test_mxfp4_gemm_validation(args, status):
     assert _lib.call("mxfp4_gemm", *args) == status
+    assert (_lib.last_error() == "") == (status == _lib.W4A4_OK)
+
+
+@pytest.mark.parametrize("args,status", [
+    # x, M, K, ldx, signs, w_codes, w_scales, N, y, ldy, stream
+    ((NUL, 4, 256, 256, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 256, 256, NUL, NUL, A, 64, A, 64, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 4, 256, 256, NUL, A, A, 64, NUL, 64, NUL), _lib.W4A4_ERR_NULL),
+    ((A, 0, 256, 256, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),      # M == 0
+    ((A, 17, 256, 256, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),     # M > 16
+    ((A, 4, 200, 200, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),      # K % 128
+    ((A, 2, 16384, 16384, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),  # K > 8192
+    ((A, 16, 8192, 8192, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),   # M * K > 65536
+    ((A, 4, 256, 128, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_SHAPE),      # ldx < K
+    ((A, 4, 256, 260, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_ALIGN),      # ldx % 8
+    ((A, 4, 256, 256, NUL, A, A, 0, A, 64, NUL), _lib.W4A4_ERR_SHAPE),       # N == 0
+    ((A, 4, 256, 256, NUL, A, A, 64, A, 63, NUL), _lib.W4A4_ERR_SHAPE),      # ldy < N
+    ((A + 2, 4, 256, 256, NUL, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_ALIGN),
+    ((A, 4, 256, 256, A + 4, A, A, 64, A, 64, NUL), _lib.W4A4_ERR_ALIGN),    # signs alignment
+])
+def test_decode_fused_validation(args, status):
+    assert _lib.call("w4a4_decode_fused", *args) == status
     assert (_lib.last_error() == "") == (status == _lib.W4A4_OK)
 
 
