@@ -283,6 +283,8 @@ def w4a4_decode_fused(x: torch.Tensor, w_codes, w_scales, signs=None, out: torch
     N = w_codes.shape[0]
     if w_codes.shape[1] * 2 != K:
         raise ValueError("x and w_codes disagree on K")
+    if w_scales.numel() != N:
+        raise ValueError("w_scales must hold one scale per output channel")
     dev = x.device
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
     _need(y, torch.float32, "out")

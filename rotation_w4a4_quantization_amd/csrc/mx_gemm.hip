@@ -257,10 +257,12 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
 
 // ---------------------------------------------------------------- decode kernel (M <= 16)
 // The product is weight-bandwidth bound: one workgroup per 16 output
-// columns, its 4 waves splitting the K steps (wave w takes steps w, w+4, ...)
-// with 8 steps of loads in flight, partial sums added through LDS.  Rows of
-// X beyond M and steps beyond K read as zero codes through the buffer range
-// checks (a zero code times any scale is zero).
+// columns, its 4 waves splitting the K steps into contiguous ranges with 8
+// steps of loads in flight, partial sums added through LDS.  A lane takes the
+// exponents of 4 consecutive steps of its row in one 16-byte load and shifts
+// out the byte of its block g per step.  Rows of X beyond M read as zero
+// codes and exponents through the buffer range check; steps beyond K are not
+// multiplied (their exponent bytes belong to the next row).
 __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
   __shared__ v4f red[3][64];
   const int tid = threadIdx.x;
@@ -268,6 +270,8 @@ __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
   const int r = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nkt = p.K / kKS;
+  const int spw = (((nkt + 3) / 4) + 3) & ~3;       // steps per wave, a multiple of 4
+  const int k_first = wave * spw;
   const int ldc = p.K / 2, lde = p.K / 32;
   const int64_t nw = p.N - n0 < 16 ? p.N - n0 : 16;
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, p.M * ldc);
@@ -275,25 +279,36 @@ __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
   const __amdgpu_buffer_rsrc_t rxe = rsrc(p.xe, p.M * lde);
   const __amdgpu_buffer_rsrc_t rwe = rsrc(p.we + n0 * lde, nw * lde);
   const int c_off = r * ldc + 16 * g;
-  const int e_off = r * lde + g;
+  const int e_off = r * lde;
+  const int gshift = 8 * g;
 
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t0 = 0; 4 * t0 < nkt; t0 += 8) {
-    uint4 xa[8], wb[8];
-    uint32_t xe[8], we[8];
+  for (int t0 = 0; t0 < spw; t0 += 8) {
+    uint4 xa[8], wb[8], xe4[2], we4[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kt = wave + 4 * (t0 + u);
-      const bool ok = kt < nkt;
-      const int co = ok ? c_off + kt * 64 : 0x7FFFFFF0;
-      const int eo = ok ? e_off + kt * 4 : 0x7FFFFFF0;
-      wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, co, 0, 0));
-      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, co, 0, 0));
-      we[u] = __builtin_amdgcn_raw_buffer_load_b8(rwe, eo, 0, 0);
-      xe[u] = __builtin_amdgcn_raw_buffer_load_b8(rxe, eo, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const int kt = k_first + t0 + 4 * h;          // exponents of steps kt .. kt + 3
+      const int eo = kt < nkt ? e_off + 4 * kt : 0x7FFFFFF0;
+      xe4[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rxe, eo, 0, 0));
+      we4[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rwe, eo, 0, 0));
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = mfma_mx<0>(xa[u], xe[u], wb[u], we[u], acc);
+    for (int u = 0; u < 8; ++u) {
+      const int kt = k_first + t0 + u;
+      const int co = (t0 + u < spw && kt < nkt) ? c_off + kt * 64 : 0x7FFFFFF0;
+      wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, co, 0, 0));
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, co, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kt = k_first + t0 + u;
+      if (t0 + u < spw && kt < nkt) {               // uniform over the wave
+        const uint4 xe = xe4[u >> 2], we = we4[u >> 2];
+        const uint32_t xd = (u & 3) == 0 ? xe.x : (u & 3) == 1 ? xe.y : (u & 3) == 2 ? xe.z : xe.w;
+        const uint32_t wd = (u & 3) == 0 ? we.x : (u & 3) == 1 ? we.y : (u & 3) == 2 ? we.z : we.w;
+        acc = mfma_mx<0>(xa[u], xd >> gshift, wb[u], wd >> gshift, acc);
+      }
+    }
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
