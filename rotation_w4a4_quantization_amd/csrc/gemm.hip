@@ -167,36 +167,26 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
   if (nkt & 1) compute(pa0, 0);
 
   // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
-  // block; after dequantizing, a quad transpose gives each lane 4 consecutive
-  // columns of one row, stored as one 16-byte write.
-  const int k4 = fr & 3;
-  const bool vec_ok = (p.ldy & 3) == 0;
+  // block; after dequantizing, pairs of blocks are stored as full 128-byte
+  // row segments.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t rb = m0 + wave * 16 * TM + 16 * i + 4 * g;
     float sx[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) sx[v] = (rb + v < p.M) ? p.xs[rb + v] : 0.0f;
-    const int64_t row = rb + k4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; j += 2) {
       const int64_t col = n0 + 16 * j + fr;
-      const float sw = col < p.N ? p.ws[col] : 0.0f;
-      float y[4];
+      const float sw0 = col < p.N ? p.ws[col] : 0.0f;
+      const float sw1 = col + 16 < p.N ? p.ws[col + 16] : 0.0f;
+      float y0[4], y1[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) y[v] = (sx[v] * sw) * (float)(acc[i][j][v] >> 8);
-      quad_transpose4(y, k4);
-      const int64_t c0 = n0 + 16 * j + (fr & ~3);     // this lane now holds row `row`, columns c0..c0+3
-      if (row < p.M) {
-        float* dst = p.y + row * p.ldy + c0;
-        if (vec_ok && c0 + 3 < p.N) {
-          store_stream4(dst, y);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (c0 + c < p.N) dst[c] = y[c];
-        }
+      for (int v = 0; v < 4; ++v) {
+        y0[v] = (sx[v] * sw0) * (float)(acc[i][j][v] >> 8);
+        y1[v] = (sx[v] * sw1) * (float)(acc[i][j + 1][v] >> 8);
       }
+      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
     }
   }
 }
@@ -390,32 +380,23 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
     fold(accB, s1);                   // group nkt - 1
   }
 
-  const int k4 = fr & 3;
-  const bool vec_ok = (p.ldy & 3) == 0;
+  // the accumulators hold 16 x the levels' products: the exact power-of-two
+  // factor is removed here, once, with the weight scale
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t row = m0 + crow[i] + k4;
+    const int64_t rb = m0 + crow[i];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; j += 2) {
       const int64_t col = n0 + 16 * j + fr;
-      // the accumulators hold 16 x the levels' products: the exact power-of-two
-      // factor is removed here, once, with the weight scale
-      const float sw = col < p.N ? p.ws[col] * 0.0625f : 0.0f;
-      float y[4];
+      const float sw0 = col < p.N ? p.ws[col] * 0.0625f : 0.0f;
+      const float sw1 = col + 16 < p.N ? p.ws[col + 16] * 0.0625f : 0.0f;
+      float y0[4], y1[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) y[v] = yf[i][j][v] * sw;
-      quad_transpose4(y, k4);
-      const int64_t c0 = n0 + 16 * j + (fr & ~3);
-      if (row < p.M) {
-        float* dst = p.y + row * p.ldy + c0;
-        if (vec_ok && c0 + 3 < p.N) {
-          store_stream4(dst, y);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (c0 + c < p.N) dst[c] = y[c];
-        }
+      for (int v = 0; v < 4; ++v) {
+        y0[v] = yf[i][j][v] * sw0;
+        y1[v] = yf[i][j + 1][v] * sw1;
       }
+      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
     }
   }
 }
@@ -497,17 +478,14 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     return hipGetLastError();
   }
   if (mode == kModeSym) {
-    // A-direct kernel.  256-row tiles of 8 waves (32 x 128 each) when there
-    // are at least two tiles per CU (two workgroups share a CU), else 256-row
-    // tiles of 16 waves (16 x 128 each) so that one workgroup per CU still
-    // has four waves per SIMD; fewer than one 256-row tile per CU: 64-row
-    // tiles of 4 waves (M = 600: 320 workgroups instead of 96).
+    // A-direct kernel.  256-row tiles of 8 waves (32 x 128 each) from one
+    // tile per CU up (measured faster than 16 waves of 16 x 128 at every
+    // shape from 256 to 511 tiles: q_proj 32.8 vs 34.8 us, 3072 x 4096 x 4096
+    // 49 vs 63 us); fewer than one 256-row tile per CU: 64-row tiles of 4
+    // waves (M = 600: 320 workgroups instead of 96).
     const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
     if (grid >= 256) {
-      if (grid >= 512)
-        W4A4_LAUNCH((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
-      else
-        W4A4_LAUNCH((gemm_adirect_kernel<16, 1, 4>), dim3((uint32_t)grid), dim3(1024), 0, st, p);
+      W4A4_LAUNCH((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
     } else {
       const int64_t grid = ((p.M + 63) / 64) * ((p.N + BN - 1) / BN);
       W4A4_LAUNCH((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);

@@ -229,28 +229,15 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   }
 
   // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
-  // block; a quad transpose gives each lane 4 consecutive columns of one
-  // row, stored as one 16-byte write.
-  const int k4 = fr & 3;
-  const bool vec_ok = (p.ldy & 3) == 0;
+  // block; pairs of blocks are stored as full 128-byte row segments.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t row = m0 + wave * 16 * TM + 16 * i + 4 * g + k4;
+    const int64_t rb = m0 + wave * 16 * TM + 16 * i + 4 * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      quad_transpose4(y, k4);
-      const int64_t c0 = n0 + 16 * j + (fr & ~3);     // this lane now holds row `row`, columns c0..c0+3
-      if (row < p.M) {
-        float* dst = p.y + row * p.ldy + c0;
-        if (vec_ok && c0 + 3 < p.N) {
-          store_stream4(dst, y);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (c0 + c < p.N) dst[c] = y[c];
-        }
-      }
+    for (int j = 0; j < 8; j += 2) {
+      float y0[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      float y1[4] = {acc[i][j + 1][0], acc[i][j + 1][1], acc[i][j + 1][2], acc[i][j + 1][3]};
+      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
     }
   }
 }
