@@ -206,6 +206,22 @@ def test_mxfp4_gemm_output_stride():
                   exact=True)
 
 
+
+@pytest.mark.parametrize("M,N,K,pad", [(40, 100, 256, 3), (2048, 4096, 128, 1), (600, 260, 256, 2)])
+def test_mxfp4_gemm_output_stride_unaligned(M, N, K, pad):
+    """Unaligned row stride and ragged N take the scalar stores of the output
+    epilogue (64-row and 256-row tilings); exact-class inputs, so the values
+    must still equal the float64 product bit for bit."""
+    s = 31 * M + N + pad
+    px, pw = WL.random_bytes(s, M, K // 2), WL.random_bytes(s + 1, N, K // 2)
+    bx, bw = WL.random_bytes(s + 2, M, K // 32, 126, 128), WL.random_bytes(s + 3, N, K // 32, 126, 128)
+    big = torch.full((M, N + pad), 7.0, dtype=torch.float32, device="cuda")
+    R.mxfp4_gemm(dev(px), dev(bx), dev(pw), dev(bw), out=big[:, :N])
+    y = host(big)
+    assert np.all(y[:, N:] == 7.0)
+    check_product(y[:, :N], mx_codes(px), bx.astype(np.int64) - 127, mx_codes(pw), bw.astype(np.int64) - 127,
+                  exact=True)
+
 def test_mxfp4_gemm_empty():
     z = torch.empty((0, 64), dtype=torch.uint8, device="cuda")
     ze = torch.empty((0, 4), dtype=torch.uint8, device="cuda")

@@ -226,6 +226,46 @@ def test_gemm_output_stride():
     assert np.all(full[:, N:] == -1.0)
 
 
+
+@pytest.mark.parametrize("M,N,K,pad", [(40, 72, 256, 3), (600, 300, 512, 5), (2048, 4096, 256, 1),
+                                       (2048, 4100, 256, 0), (513, 4096, 384, 2)])
+def test_gemm_output_stride_unaligned(M, N, K, pad):
+    """Row strides that are not a multiple of 4 floats, and ragged N, take the
+    scalar stores of the output epilogue (64-row and 256-row tilings); the
+    values still match the oracle's fp32 epilogue bit for bit and nothing past
+    column N is written."""
+    qa, qb = _rand_codes(M + 7, M, K), _rand_codes(N + 11, N, K)
+    rng = np.random.default_rng(M * N + pad)
+    sx = (rng.random(M) * 2 + 0.01).astype(np.float32)
+    sw = (rng.random(N) * 0.01 + 1e-4).astype(np.float32)
+    buf = torch.full((M, N + pad), -1.0, device="cuda")
+    R.w4a4_gemm(dev(O.pack_nibbles(qa)), dev(sx), None, dev(O.pack_nibbles(qb)), dev(sw), out=buf[:, :N])
+    full = host(buf)
+    assert np.array_equal(full[:, :N], O.epilogue_sym_f32(O.int_gemm(qa, qb), sx, sw))
+    assert np.all(full[:, N:] == -1.0)
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(130, 260, 256, 3), (300, 129, 384, 1)])
+def test_gemm_asym_output_stride_unaligned(M, N, K, pad):
+    """Asymmetric kernel, unaligned row stride: the same values as a
+    contiguous output (only the store addresses differ), within the oracle's
+    tolerance, and nothing past column N is written."""
+    rng = np.random.default_rng(M + N + K + pad)
+    G = K // 128
+    u = rng.integers(0, 16, (M, K))
+    zp = rng.integers(0, 16, (M, G))
+    qw = _rand_codes(N + 5, N, K)
+    sx = (rng.random((M, G)) + 0.05).astype(np.float32)
+    sw = (rng.random(N) * 0.01 + 1e-4).astype(np.float32)
+    args = (dev(O.pack_nibbles(u)), dev(sx), dev(zp.astype(np.uint8)), dev(O.pack_nibbles(qw)), dev(sw))
+    y = host(R.w4a4_gemm(*args, act_mode="asym"))
+    buf = torch.full((M, N + pad), -1.0, device="cuda")
+    R.w4a4_gemm(*args, act_mode="asym", out=buf[:, :N])
+    full = host(buf)
+    assert np.array_equal(full[:, :N], y)
+    assert np.all(full[:, N:] == -1.0)
+    assert rel_fro(y, O.gemm_asym_f64(u, zp, sx, qw, sw)) < 1e-6
+
 # ---------------------------------------------------------------- end to end
 def _e2e(x, w, block, mode="sym"):
     hb = block if block == 128 else "full"
