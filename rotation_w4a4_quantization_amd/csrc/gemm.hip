@@ -309,6 +309,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
     v4i a[TM][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
       const uint32_t bias = (128u - z[i]) * 0x01010101u;
       const uint32_t w[4] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w};
       uint32_t o[8];
@@ -341,6 +342,11 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 #pragma unroll
         for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sf[i][v], (float)acc[i][j][v], yf[i][j][v]);
   };
+
+  // Group g's codes and zero-points sit in register set g & 1 and its scales
+  // in set g & 1 too; group g's step folds group g-1 with the scales of set
+  // (g-1) & 1, which is refilled right afterwards with group g+1's codes,
+  // zero-points and scales (one group ahead).  Set 1 starts with zero scales.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
