@@ -26,10 +26,18 @@ function that uses it):
     zero-point = round(-lo/s), code = round(y/s) + zero-point.
   * Round to nearest, ties to even; an all-zero row or group gets scale 0,
     zero-point 0 and codes 0.
-  * Where floating point decides a code, the decision is taken in fp32 the
-    way the GPU kernel takes it: the rotated value rounded once to fp32, the
-    reciprocal scale fp32, their product exact (held in float64), then
-    rounded to the nearest integer.
+  * Codes are decided from the plain definition in float64 (mode "f64", the
+    default): the exact rotated value z, t = 7 z / max|z| (symmetric) or
+    t = 15 z / (hi - lo) (asymmetric), rounded to nearest.  The rotation of
+    fp16 inputs is exact in float64, so t carries only the rounding of one
+    or two float64 operations.
+  * A second mode, "f32", evaluates the same formulas in IEEE fp32 with
+    correctly rounded division: z rounded once to fp32, the reciprocal
+    scale in fp32, their product exact, then rounded to the nearest
+    integer.  It exists for inputs whose fp32 rotation is exact (integer
+    fp16 values of moderate size), where a GPU that follows that fp32
+    formula must reproduce its codes and scales bit for bit.  Outside that
+    class the two modes differ only within a few fp32 ulps of a .5 tie.
 """
 from __future__ import annotations
 
@@ -109,22 +117,36 @@ def _rne(t: np.ndarray) -> np.ndarray:
     return np.rint(t)
 
 
-def quant_sym_rows(z, block: int) -> dict:
+def quant_sym_rows(z, block: int, mode: str = "f64") -> dict:
     """Symmetric INT4, one scale per row, on unnormalized rotated rows z.
 
     [ROT] "What it buys in 4 bits": INT4 with one scale per token for the
     activations and one per output channel for the weights.  The normalized
     rotated row is y = z / sqrt(block) (block = 1: no rotation).
-    Reading: 15 levels, s = max|y| / 7, q = round(y / s) clamped to [-7, 7].
+    Reading: 15 levels, s = max|y| / 7, q = round(y / s) clamped to [-7, 7],
+    round to nearest with ties to even ([ROT] "Gotchas": round to nearest).
 
     Since y / s = 7 z / max|z|, the code does not depend on the block; it only
     enters the stored scale:  s = max|z| / (7 sqrt(block)).
 
-    fp32 decision (matches the kernel): a = max|fl32(z)|,
-    s = fl32(a / fl32(7 sqrt(block))), inv = fl32(7 / a),
-    t = fl32(z) * inv exactly, q = rne(t).  Returned `t` is that pre-rounding
-    value, used by tests to locate ties.
+    mode "f64" (the definition): a = max|z|, s = a / (7 sqrt(block)),
+    t = 7 z / a, q = rne(t), all in float64; a = 0 gives s = 0 and q = 0.
+    mode "f32" (exact-fp32 form): a = max|fl32(z)|,
+    s = fl32(a / fl32(7 sqrt(block))), inv = fl32(7 / a), t = fl32(z) * inv
+    held exactly, q = rne(t).
+    Returned `t` is the pre-rounding value of the chosen mode.
     """
+    if mode == "f64":
+        zz = np.asarray(z, dtype=F64)
+        a = np.max(np.abs(zz), axis=1)
+        nz = a > 0
+        safe = np.where(nz, a, 1.0)
+        s = np.where(nz, a / (7.0 * np.sqrt(F64(block))), 0.0)
+        t = np.where(nz[:, None], 7.0 * zz / safe[:, None], 0.0)
+        q = np.clip(_rne(t), -7, 7).astype(np.int8)
+        return dict(codes=q, scale=s, t=t, absmax=a, mode=mode)
+    if mode != "f32":
+        raise ValueError(mode)
     z32 = np.asarray(z, dtype=F64).astype(F32)
     a = np.max(np.abs(z32), axis=1)                       # fp32, exact
     c = F32(7.0 * np.sqrt(F64(block)))
@@ -134,10 +156,10 @@ def quant_sym_rows(z, block: int) -> dict:
     inv = np.where(nz, F32(7.0) / safe, F32(0)).astype(F32)
     t = z32.astype(F64) * inv.astype(F64)[:, None]       # product of two fp32: exact in f64
     q = np.clip(_rne(t), -7, 7).astype(np.int8)
-    return dict(codes=q, scale=s, inv=inv, t=t, absmax=a)
+    return dict(codes=q, scale=s, inv=inv, t=t, absmax=a, mode=mode)
 
 
-def quant_asym_groups(z, block: int, group: int = 128) -> dict:
+def quant_asym_groups(z, block: int, group: int = 128, mode: str = "f64") -> dict:
     """Asymmetric INT4 with a zero-point, one (scale, zero-point) per group.
 
     [SQ] "Activation scheme": per-group asymmetric INT4 for weights,
@@ -149,28 +171,49 @@ def quant_asym_groups(z, block: int, group: int = 128) -> dict:
     dequantized value s * (q - zp).  As in `quant_sym_rows`, the codes depend
     on z only and sqrt(block) enters the scale alone.
 
-    fp32 decision: r = fl32(hi - lo), s = fl32(r / fl32(15 sqrt(block))),
-    inv = fl32(15 / r), the products -lo*inv and z*inv exact, then rne.
+    mode "f64" (the definition): r = hi - lo, s = r / (15 sqrt(block)),
+    t = 15 z / r, t_zp = -15 lo / r, all in float64.
+    mode "f32": r = fl32(hi - lo), s = fl32(r / fl32(15 sqrt(block))),
+    inv = fl32(15 / r), the products -lo*inv and z*inv held exactly.
+    Either way zp = clamp(rne(t_zp), 0, 15), q = clamp(rne(t) + zp, 0, 15)
+    (the integer add comes after rounding); r = 0 gives s = 0, zp = 0, q = 0.
     """
-    z32 = np.asarray(z, dtype=F64).astype(F32)
-    R, K = z32.shape
+    if mode == "f64":
+        zz = np.asarray(z, dtype=F64)
+    elif mode == "f32":
+        zz = np.asarray(z, dtype=F64).astype(F32)
+    else:
+        raise ValueError(mode)
+    R, K = zz.shape
     if K % group:
         raise ValueError("K must be a multiple of the group width")
-    g = z32.reshape(R, K // group, group)
-    lo = np.minimum(g.min(axis=2), F32(0))
-    hi = np.maximum(g.max(axis=2), F32(0))
-    r = (hi - lo).astype(F32)                                # correctly rounded fp32 subtraction
-    c = F32(15.0 * np.sqrt(F64(block)))
-    nz = r > 0
-    safe = np.where(nz, r, F32(1))
-    s = np.where(nz, safe / c, F32(0)).astype(F32)
-    inv = np.where(nz, F32(15.0) / safe, F32(0)).astype(F32)
-    t_zp = (-lo).astype(F64) * inv.astype(F64)
+    g = zz.reshape(R, K // group, group)
+    lo = np.minimum(g.min(axis=2), 0)
+    hi = np.maximum(g.max(axis=2), 0)
+    if mode == "f64":
+        r = hi - lo
+        nz = r > 0
+        safe = np.where(nz, r, 1.0)
+        s = np.where(nz, r / (15.0 * np.sqrt(F64(block))), 0.0)
+        t_zp = np.where(nz, -15.0 * lo / safe, 0.0)
+        t = np.where(nz[:, :, None], 15.0 * g / safe[:, :, None], 0.0)
+        inv = None
+    else:
+        r = (hi - lo).astype(F32)                            # correctly rounded fp32 subtraction
+        c = F32(15.0 * np.sqrt(F64(block)))
+        nz = r > 0
+        safe = np.where(nz, r, F32(1))
+        s = np.where(nz, safe / c, F32(0)).astype(F32)
+        inv = np.where(nz, F32(15.0) / safe, F32(0)).astype(F32)
+        t_zp = (-lo).astype(F64) * inv.astype(F64)
+        t = g.astype(F64) * inv.astype(F64)[:, :, None]
     zp = np.clip(_rne(t_zp), 0, 15)
-    t = g.astype(F64) * inv.astype(F64)[:, :, None]
     q = np.clip(_rne(t) + zp[:, :, None], 0, 15).astype(np.uint8)
-    return dict(codes=q.reshape(R, K), scale=s, zp=zp.astype(np.uint8), inv=inv,
-                t=t.reshape(R, K), t_zp=t_zp, lo=lo, hi=hi)
+    d = dict(codes=q.reshape(R, K), scale=s, zp=zp.astype(np.uint8),
+             t=t.reshape(R, K), t_zp=t_zp, lo=lo, hi=hi, mode=mode)
+    if inv is not None:
+        d["inv"] = inv
+    return d
 
 
 def dequant_sym_rows(q, s) -> np.ndarray:
@@ -290,21 +333,22 @@ def int_gemm_groups(u, zp, qw, group: int = 128) -> np.ndarray:
 # --------------------------------------------------------------------------
 # End-to-end pieces of the path
 # --------------------------------------------------------------------------
-def rotate_quant_act(x, block: int, mode: str, signs=None) -> dict:
+def rotate_quant_act(x, block: int, mode: str, signs=None, decide: str = "f64") -> dict:
     """Online activation step: rotate each token, quantize, pack.
 
     [ROT] "Where the rotations go": rotations that cannot be folded into the
     weights cost one fast Hadamard transform per token, fused with the
     quantization of the activations.  mode "sym": one scale per token;
     mode "asym": asymmetric per group of 128 with a zero-point.  signs: the
-    randomized-Hadamard diagonal (see `apply_signs`), or None.
+    randomized-Hadamard diagonal (see `apply_signs`), or None.  decide: the
+    quantizer's arithmetic, "f64" (the definition) or "f32" (exact-fp32 form).
     """
     z = rotate(x, block, signs)
     if mode == "sym":
-        d = quant_sym_rows(z, block)
+        d = quant_sym_rows(z, block, decide)
         d["packed"] = pack_nibbles(d["codes"])
     elif mode == "asym":
-        d = quant_asym_groups(z, block, 128)
+        d = quant_asym_groups(z, block, 128, decide)
         d["packed"] = pack_nibbles(d["codes"])
     else:
         raise ValueError(mode)
@@ -312,30 +356,30 @@ def rotate_quant_act(x, block: int, mode: str, signs=None) -> dict:
     return d
 
 
-def quant_weight_offline(w, block: int, signs=None) -> dict:
+def quant_weight_offline(w, block: int, signs=None, decide: str = "f64") -> dict:
     """Offline weight step: rotate each output channel's row, symmetric INT4
     per output channel, pack, and the per-128 group sums of the codes.
 
     [ROT] "Where the rotations go": rotations applied to weights are folded
     offline and cost nothing at run time.  signs: the same diagonal the
-    activations use, or None.
+    activations use, or None.  decide: as in `rotate_quant_act`.
     """
     z = rotate(w, block, signs)
-    d = quant_sym_rows(z, block)
+    d = quant_sym_rows(z, block, decide)
     d["packed"] = pack_nibbles(d["codes"])
     d["gsum"] = group_sums(d["codes"], 128)
     d["z"] = z
     return d
 
 
-def w4a4_linear(x, w, block: int, mode: str = "sym", signs=None) -> dict:
+def w4a4_linear(x, w, block: int, mode: str = "sym", signs=None, decide: str = "f64") -> dict:
     """Y_hat = Q(XQ) . Q(WQ)^T and the float64 X W^T it approximates.
 
     [ROT] "A rotation changes nothing" (invariance) and "What it buys in 4
     bits" (the quantized product).
     """
-    a = rotate_quant_act(x, block, mode, signs)
-    wq = quant_weight_offline(w, block, signs)
+    a = rotate_quant_act(x, block, mode, signs, decide)
+    wq = quant_weight_offline(w, block, signs, decide)
     if mode == "sym":
         acc = int_gemm(a["codes"], wq["codes"])
         y = epilogue_sym_f64(acc, a["scale"], wq["scale"])
@@ -345,20 +389,21 @@ def w4a4_linear(x, w, block: int, mode: str = "sym", signs=None) -> dict:
     return dict(act=a, wq=wq, acc=acc, y=y)
 
 
-def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
+def kv_rotate_quant(kv, block: int = 128, signs=None, decide: str = "f64") -> dict:
     """KV cache step: rotate every (batch, head, token) vector of head_dim 128
     with one 128-point Hadamard, then asymmetric INT4 with a zero-point, one
     group per vector.
 
     [QR] "Activation scheme": the KV cache is rotated as well;
     [SQ] "Activation scheme": per-group asymmetric INT4 on the KV cache.
+    decide: as in `rotate_quant_act`.
     """
     kv = np.asarray(kv)
     shape = kv.shape
     D = shape[-1]
     flat = kv.reshape(-1, D)
     z = rotate(flat, block, signs)
-    d = quant_asym_groups(z, block, D)
+    d = quant_asym_groups(z, block, D, decide)
     d["packed"] = pack_nibbles(d["codes"]).reshape(*shape[:-1], D // 2)
     d["scale"] = d["scale"].reshape(shape[:-1])
     d["zp"] = d["zp"].reshape(shape[:-1])
@@ -378,8 +423,9 @@ def kv_rotate_quant(kv, block: int = 128, signs=None) -> dict:
 # stored as the biased byte e + 127; elements round to nearest on the grid,
 # ties to the even code, and saturate at +-6.  A block of zeros gets the
 # byte 0 and zero codes.  What is quantized is the normalized rotated value
-# y = x Q (the scale is a power of two, so 1/sqrt(b) matters here), formed in
-# fp32 as the kernel forms it: y = fl32(fl32(z) * fl32(1/sqrt(b))).
+# y = x Q = z / sqrt(b) (the scale is a power of two, so 1/sqrt(b) matters
+# here), in float64; the exact-fp32 form y = fl32(fl32(z) * fl32(1/sqrt(b)))
+# is the second mode, for inputs whose fp32 rotation is exact.
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 MX_BLOCK = 32
 
@@ -410,13 +456,13 @@ def e2m1_round(t) -> np.ndarray:
     return (mag + 8 * neg).astype(np.int64)
 
 
-def mx_quant_rows(y32, block: int = MX_BLOCK) -> dict:
-    """MXFP4 quantization of fp32 rows y32 [R, K] in blocks of 32 along K.
+def mx_quant_rows(y, block: int = MX_BLOCK) -> dict:
+    """MXFP4 quantization of rows y [R, K] (float64 values) in blocks of 32 along K.
 
     Returns codes [R, K] (0..15), scale_e [R, K/32] (the exponent e) and
     scale_byte (e + 127).
     """
-    y = np.asarray(y32, dtype=F32).astype(F64)
+    y = np.asarray(y, dtype=F64)
     R, K = y.shape
     yb = y.reshape(R, K // block, block)
     amax = np.abs(yb).max(axis=-1)
@@ -435,17 +481,27 @@ def mx_dequant_rows(codes, scale_e, block: int = MX_BLOCK) -> np.ndarray:
     return (v * np.exp2(np.asarray(scale_e, dtype=F64))[..., None]).reshape(R, K)
 
 
-def rotate_mx_quant(x, block: int, signs=None) -> dict:
+def rotate_mx_quant(x, block: int, signs=None, decide: str = "f64") -> dict:
     """Rotate each row (Q = diag(d) H_block / sqrt(block)), then MXFP4.
 
     [ROT] "The full model in NVFP4, on vLLM" and "When to rotate": rotations
-    help MXFP4, whose scales are powers of two shared by 32 values.  Codes are packed two per byte like the INT4 codes.
+    help MXFP4, whose scales are powers of two shared by 32 values.  Codes
+    are packed two per byte like the INT4 codes.
+    decide "f64": y = z / sqrt(block) in float64 (the definition);
+    "f32": y = fl32(fl32(z) * fl32(1 / sqrt(block))).  Returned `y` is the
+    value that was quantized.
     """
     z = rotate(x, block, signs)
-    y32 = (z.astype(F32) * F32(1.0 / np.sqrt(block))).astype(F32)
-    d = mx_quant_rows(y32)
+    if decide == "f64":
+        y = z / np.sqrt(F64(block))
+    elif decide == "f32":
+        y = (z.astype(F32) * F32(1.0 / np.sqrt(block))).astype(F32).astype(F64)
+    else:
+        raise ValueError(decide)
+    d = mx_quant_rows(y)
     d["packed"] = pack_nibbles(d["codes"])
-    d["y32"] = y32
+    d["y"] = y
+    d["mode"] = decide
     return d
 
 

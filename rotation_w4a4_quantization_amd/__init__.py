@@ -130,31 +130,76 @@ def quant_weight_offline(w: torch.Tensor, had_block: int = 128, with_gsum: bool 
     return codes, scales, gsum
 
 
-def w4a4_gemm(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum=None, act_mode: str = "sym",
-              out: torch.Tensor | None = None):
-    """Y fp32 [M, N] from packed INT4 activations and weights (see include/w4a4.h)."""
-    _need(x_codes, torch.uint8, "x_codes")
-    _need(w_codes, torch.uint8, "w_codes")
-    _need(x_scales, torch.float32, "x_scales")
-    _need(w_scales, torch.float32, "w_scales")
-    mode = _MODES[act_mode]
-    if x_zeros is not None:
-        _need(x_zeros, torch.uint8, "x_zeros")
-    for t, n in ((x_codes, "x_codes"), (w_codes, "w_codes"), (x_scales, "x_scales"),
-                 (w_scales, "w_scales")):
+def _gemm_operands(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum, mode: int):
+    """Dtype, shape and layout of the GEMM operands, checked before any
+    device work (the kernels size their reads from M, N and K, not from the
+    tensors, so a short scale vector would be read past its end).  Returns
+    (M, N, K)."""
+    for t, n, dt in ((x_codes, "x_codes", torch.uint8), (w_codes, "w_codes", torch.uint8),
+                     (x_scales, "x_scales", torch.float32), (w_scales, "w_scales", torch.float32)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{n} must be {dt}, got {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
+    if x_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("x_codes and w_codes must be 2-D [rows, K/2]")
     M, K2 = x_codes.shape
     N = w_codes.shape[0]
     if w_codes.shape[1] != K2:
         raise ValueError("x_codes and w_codes disagree on K")
+    K = 2 * K2
+    G = K // 128
+    if tuple(w_scales.shape) != (N,):
+        raise ValueError(f"w_scales must be [N] = [{N}], got {tuple(w_scales.shape)}")
+    if mode == W4A4_ACT_SYM_TOKEN:
+        if tuple(x_scales.shape) != (M,):
+            raise ValueError(f"symmetric x_scales must be [M] = [{M}], got {tuple(x_scales.shape)}")
+        if x_zeros is not None:
+            raise ValueError("x_zeros must be None in symmetric mode")
+    else:
+        if tuple(x_scales.shape) != (M, G):
+            raise ValueError(f"asymmetric x_scales must be [M, K/128] = [{M}, {G}], got {tuple(x_scales.shape)}")
+        if not isinstance(x_zeros, torch.Tensor):
+            raise ValueError("asymmetric mode needs x_zeros [M, K/128]")
+        if x_zeros.dtype != torch.uint8:
+            raise TypeError(f"x_zeros must be {torch.uint8}, got {x_zeros.dtype}")
+        if tuple(x_zeros.shape) != (M, G) or not x_zeros.is_contiguous():
+            raise ValueError(f"x_zeros must be a contiguous [M, K/128] = [{M}, {G}] tensor")
+    if w_gsum is not None:
+        if not isinstance(w_gsum, torch.Tensor) or w_gsum.dtype != torch.int32:
+            raise TypeError("w_gsum must be an int32 tensor")
+        if tuple(w_gsum.shape) != (N, G) or not w_gsum.is_contiguous():
+            raise ValueError(f"w_gsum must be a contiguous [N, K/128] = [{N}, {G}] tensor")
+    return M, N, K
+
+
+def w4a4_gemm(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum=None, act_mode: str = "sym",
+              out: torch.Tensor | None = None):
+    """Y fp32 [M, N] from packed INT4 activations and weights (see include/w4a4.h).
+
+    Symmetric: x_scales [M], x_zeros None.  Asymmetric: x_scales and x_zeros
+    [M, K/128].  w_scales [N]; w_gsum (optional) [N, K/128].
+    """
+    mode = _MODES[act_mode]
+    M, N, K = _gemm_operands(x_codes, x_scales, x_zeros, w_codes, w_scales, w_gsum, mode)
     dev = x_codes.device
+    for t, n in ((x_codes, "x_codes"), (w_codes, "w_codes"), (x_scales, "x_scales"),
+                 (w_scales, "w_scales"), (x_zeros, "x_zeros"), (w_gsum, "w_gsum")):
+        if t is not None:
+            if not t.is_cuda:
+                raise TypeError(f"{n} must be a CUDA (HIP) tensor")
+            if t.device != dev:
+                raise ValueError(f"{n} must be on the same device as x_codes")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
     _need(y, torch.float32, "out")
     if y.dim() != 2 or y.shape[0] != M or y.shape[1] != N or y.stride(1) != 1:
         raise ValueError("out must be [M, N] with contiguous rows")
+    if y.device != dev:
+        raise ValueError("out must be on the same device as x_codes")
     st = _lib.call("w4a4_gemm", _ptr(x_codes), _ptr(x_scales), _ptr(x_zeros), mode, _ptr(w_codes),
-                   _ptr(w_scales), _ptr(w_gsum), M, N, 2 * K2, _ptr(y), y.stride(0), _stream(dev))
+                   _ptr(w_scales), _ptr(w_gsum), M, N, K, _ptr(y), y.stride(0), _stream(dev))
     _check(st, "w4a4_gemm")
     return y
 

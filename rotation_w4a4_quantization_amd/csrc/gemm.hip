@@ -254,8 +254,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   }
 
   // A codes, zero-points and the C rows' scales of a K step travel together,
-  // two steps ahead of their use; all are buffer loads (no branches, so no
-  // wait is forced until the step that consumes them)
+  // loaded one group ahead of their use (right after the step before it);
+  // all are buffer loads (no branches, so no wait is forced until the step
+  // that consumes them)
   uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
   uint32_t z0[TM], z1[TM];
   float s0[TM][4], s1[TM][4];

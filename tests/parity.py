@@ -1,10 +1,12 @@
 """GPU-vs-oracle comparison rules (test helper).
 
-Codes may differ from the oracle's only where the oracle's pre-rounding value
-t lies within TIE_WINDOW of a .5 tie (the GPU transform runs in fp32, the
+Codes may differ from the oracle's only where the oracle's float64
+pre-rounding value t (the plain definition, t = 7 z / max|z| or 15 z / r)
+lies within TIE_WINDOW of a .5 tie (the GPU transform runs in fp32, the
 oracle's exactly), by one level, and at most MAX_FLIP_FRAC of the elements.
 Packed bytes must agree wherever both of their codes agree.  Scales agree to
-SCALE_RTOL relative (bit-exact on the exact-arithmetic inputs).
+SCALE_RTOL relative.  On the exact-arithmetic inputs the GPU must instead
+equal the oracle's exact-fp32 mode bit for bit (codes, scales, bytes).
 """
 from __future__ import annotations
 
@@ -29,7 +31,10 @@ def ulp_diff(a: np.ndarray, b: np.ndarray) -> int:
 
 
 def check_sym(packed_gpu, scales_gpu, ref: dict, exact: bool = False) -> dict:
-    """Compare GPU symmetric codes/scales with oracle `quant_sym_rows` output."""
+    """Compare GPU symmetric codes/scales with oracle `quant_sym_rows` output:
+    the float64 mode under the tie rule, or (exact=True) the exact-fp32 mode
+    bit for bit."""
+    assert ref["mode"] == ("f32" if exact else "f64"), "wrong oracle mode for this comparison"
     q_gpu = O.unpack_nibbles(packed_gpu, signed=True)
     q_ref = ref["codes"].astype(np.int64)
     assert q_gpu.shape == q_ref.shape
@@ -50,7 +55,9 @@ def check_sym(packed_gpu, scales_gpu, ref: dict, exact: bool = False) -> dict:
 
 
 def check_asym(packed_gpu, scales_gpu, zeros_gpu, ref: dict, exact: bool = False) -> dict:
-    """Compare GPU asymmetric codes/scales/zero-points with `quant_asym_groups` output."""
+    """Compare GPU asymmetric codes/scales/zero-points with `quant_asym_groups`
+    output (float64 mode under the tie rule, or exact-fp32 mode bit for bit)."""
+    assert ref["mode"] == ("f32" if exact else "f64"), "wrong oracle mode for this comparison"
     R = ref["codes"].shape[0]
     G = ref["zp"].shape[1]
     u_gpu = O.unpack_nibbles(packed_gpu.reshape(R, -1), signed=False)
@@ -114,8 +121,10 @@ def check_mx(packed_gpu, sbytes_gpu, ref: dict, exact: bool = False) -> dict:
     An exponent may differ (by one) only where the oracle's block maximum is
     within TIE_WINDOW of a power of two; codes are then checked against the
     oracle's rounding under the GPU's exponent, and may differ (by one
-    magnitude step) only near an E2M1 midpoint."""
-    y = np.asarray(ref["y32"], np.float64)
+    magnitude step) only near an E2M1 midpoint.  `ref` is the float64 mode,
+    or (exact=True) the exact-fp32 mode, which must match bit for bit."""
+    assert ref["mode"] == ("f32" if exact else "f64"), "wrong oracle mode for this comparison"
+    y = np.asarray(ref["y"], np.float64)
     R, K = y.shape
     J = K // 32
     e_ref = np.asarray(ref["scale_e"], np.int64)

@@ -84,7 +84,8 @@ def test_rotate_quant_mxfp4_exact_class(K, block):
     z * fl32(1/sqrt(b)) on both sides, so codes and exponents match bit for bit."""
     x = WL.exact_class(K + 3 * block, 48, K, lim=2048, outlier_cols=[7, K // 2])
     c, e = gpu_mx(x, "full" if block == K and K > 128 else 128)
-    check_mx(c, e, O.rotate_mx_quant(x, block), exact=True)
+    check_mx(c, e, O.rotate_mx_quant(x, block, decide="f32"), exact=True)
+    check_mx(c, e, O.rotate_mx_quant(x, block))
 
 
 def test_rotate_quant_mxfp4_exact_midpoints():
@@ -109,10 +110,12 @@ def test_rotate_quant_mxfp4_exact_midpoints():
     x64 = O.rotate(c, K)                       # H c (the unnormalized transform)
     x = x64.astype(np.float16)
     assert np.array_equal(x.astype(np.float64), x64), "H c must be exact in fp16"
-    ref = O.rotate_mx_quant(x, K)
+    ref = O.rotate_mx_quant(x, K, decide="f32")
     assert np.all(ref["scale_e"] == 5)
-    t = ref["y32"].astype(np.float64) / 32.0
+    t = ref["y"] / 32.0
     assert np.array_equal(t, c)
+    # 1/sqrt(1024) is a power of two, so the float64 definition gives the same y
+    assert np.array_equal(O.rotate_mx_quant(x, K)["y"], ref["y"])
     n_ties = int(np.isin(np.abs(t), mids).sum())
     assert n_ties >= 3 * rows * (K // 32)
     cg, eg = gpu_mx(x, "full")

@@ -46,7 +46,9 @@ def test_signed_exact_class_bitexact(K, block):
     x = WL.exact_class(K + 1, 48, K, lim=2048, outlier_cols=[3, K // 2])
     d = WL.hadamard_signs(K, seed=7)
     c, s, _ = R.rotate_quant_act(dev(x), 128 if block == 128 else "full", signs=dev(d))
-    check_sym(host(c), host(s), O.quant_sym_rows(O.rotate(x, block, d), block), exact=True)
+    z = O.rotate(x, block, d)
+    check_sym(host(c), host(s), O.quant_sym_rows(z, block, "f32"), exact=True)
+    check_sym(host(c), host(s), O.quant_sym_rows(z, block))
 
 
 def test_all_plus_signs_equal_no_signs():

@@ -127,9 +127,12 @@ def test_outlier_spreads_evenly(n, j, m):
     y = O.rotate_normalized(x, n)[0]
     pc = np.array([bin(j & i).count("1") for i in range(n)])
     assert np.allclose(y, m / math.sqrt(n) * np.where(pc % 2 == 0, 1, -1), rtol=1e-15, atol=0)
-    q = O.quant_sym_rows(O.rotate(x, n), n)
-    assert np.array_equal(q["codes"][0], 7 * np.sign(m) * np.where(pc % 2 == 0, 1, -1))
-    # s = max|y| / 7 = |M| / (7 sqrt(n))
+    for mode in ("f64", "f32"):
+        q = O.quant_sym_rows(O.rotate(x, n), n, mode)
+        assert np.array_equal(q["codes"][0], 7 * np.sign(m) * np.where(pc % 2 == 0, 1, -1))
+    # s = max|y| / 7 = |M| / (7 sqrt(n)); in the fp32 form one division of fp32 values
+    assert math.isclose(O.quant_sym_rows(O.rotate(x, n), n)["scale"][0], abs(m) / (7 * math.sqrt(n)),
+                        rel_tol=4e-16)
     assert q["scale"][0] == np.float32(abs(m)) / np.float32(7 * math.sqrt(n))
 
 
@@ -156,17 +159,19 @@ def test_quant_worked_examples():
         if kind == "sym":
             _, zs, qs, ss, bs = [p.strip() for p in ln.split("|")]
             z = np.array([[float(v) for v in zs.split()]])
-            d = O.quant_sym_rows(z, 1)
-            assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
-            assert d["scale"][0] == np.float32(float(ss)), ln
-            assert O.pack_nibbles(d["codes"])[0].tolist() == [int(b, 16) for b in bs.split()], ln
+            for mode in ("f64", "f32"):
+                d = O.quant_sym_rows(z, 1, mode)
+                assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
+                assert d["scale"][0] == float(ss), ln
+                assert O.pack_nibbles(d["codes"])[0].tolist() == [int(b, 16) for b in bs.split()], ln
         elif kind == "asym":
             _, zs, qs, ss, zps = [p.strip() for p in ln.split("|")]
             z = np.array([[float(v) for v in zs.split()]])
-            d = O.quant_asym_groups(z, 1, group=z.shape[1])
-            assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
-            assert d["scale"][0, 0] == np.float32(float(ss)), ln
-            assert d["zp"][0, 0] == int(zps), ln
+            for mode in ("f64", "f32"):
+                d = O.quant_asym_groups(z, 1, group=z.shape[1], mode=mode)
+                assert d["codes"][0].tolist() == [int(v) for v in qs.split()], ln
+                assert d["scale"][0, 0] == float(ss), ln
+                assert d["zp"][0, 0] == int(zps), ln
 
 
 def _brute_code(t, lo, hi):
@@ -180,23 +185,110 @@ def _brute_code(t, lo, hi):
 
 
 def test_sym_codes_brute_force():
-    z = O.rotate(WL.small_random(4, 6, 256, outlier_cols=[9], mult=50.0), 128)
+    """Codes of the float64 mode = the nearest level to the exact rational
+    7 z / max|z| (z exact for fp16 inputs), by exhaustive search in Fraction."""
+    x = WL.small_random(4, 6, 256, outlier_cols=[9], mult=50.0)
+    z = O.rotate(x, 128)
     d = O.quant_sym_rows(z, 128)
     for r in range(6):
+        zr = [Fraction(float(v)) for v in z[r]]
+        a = max(abs(v) for v in zr)
         for k in range(256):
-            assert d["codes"][r, k] == _brute_code(d["t"][r, k], -7, 7)
+            assert d["codes"][r, k] == _brute_code(7 * zr[k] / a, -7, 7)
+        assert d["scale"][r] == float(a) / (7 * math.sqrt(128))
 
 
 def test_asym_levels_brute_force():
+    """Zero-points and codes of the float64 mode from the exact rationals
+    -15 lo / r and 15 z / r, r = hi - lo with the range widened to include 0."""
     z = O.rotate(WL.small_random(5, 4, 256, outlier_cols=[2], mult=20.0), 128)
     d = O.quant_asym_groups(z, 128)
     for r in range(4):
         for g in range(2):
+            grp = [Fraction(float(v)) for v in z[r, g * 128:(g + 1) * 128]]
+            lo, hi = min(min(grp), Fraction(0)), max(max(grp), Fraction(0))
+            rng_ = hi - lo
             zp = int(d["zp"][r, g])
-            assert zp == _brute_code(d["t_zp"][r, g], 0, 15)
+            assert zp == _brute_code(-15 * lo / rng_, 0, 15)
             for k in range(128):
-                lvl = _brute_code(d["t"][r, g * 128 + k], -100, 100)
+                lvl = _brute_code(15 * grp[k] / rng_, -100, 100)
                 assert d["codes"][r, g * 128 + k] == min(max(lvl + zp, 0), 15)
+
+
+def _dist_to_tie(t):
+    return np.abs(np.abs(t - np.floor(t)) - 0.5)
+
+
+# fp32 rounding budget of the exact-fp32 form against the definition: the
+# symmetric t32 = fl32(z) * fl32(7 / fl32(a)) carries three relative
+# roundings of at most 2^-24 each; the asymmetric one four (fl32 of z, of hi
+# or lo, of hi - lo, of 15 / r).  The float64 evaluation adds a few 2^-53.
+SYM_T_BUDGET = 3.001 * 2.0 ** -24
+ASYM_T_BUDGET = 4.001 * 2.0 ** -24
+
+
+def test_decision_modes_at_an_exact_tie():
+    """Hand-worked: z = (42, 3), block 1.  The definition gives t = 7*3/42 = 1/2
+    exactly, which rounds half to even: code 0.  The exact-fp32 form uses
+    fl32(7/42) = fl32(1/6) = 11184811 * 2^-26 > 1/6, so t32 = 3 * that > 1/2
+    and the code is 1 (-1 for z = -3).  This is the only kind of place where
+    the two modes may differ, and the GPU-vs-oracle tie window covers it."""
+    z = np.array([[42.0, 3.0], [42.0, -3.0]])
+    d64, d32 = O.quant_sym_rows(z, 1), O.quant_sym_rows(z, 1, "f32")
+    assert d64["t"][0, 1] == 0.5 and d64["codes"].tolist() == [[7, 0], [7, 0]]
+    assert np.float32(1 / 6) == np.float32(11184811 * 2.0 ** -26)
+    assert d32["t"][0, 1] == 3 * 11184811 * 2.0 ** -26 and d32["codes"].tolist() == [[7, 1], [7, -1]]
+
+
+@pytest.mark.parametrize("cfg,block", [("qproj", 128), ("qproj", 4096), ("downproj", 128)])
+def test_decision_modes_agree_off_ties_sym(cfg, block):
+    """The exact-fp32 form decides every code as the float64 definition does,
+    except within its rounding budget (|t| * 3 * 2^-24 <= 1.26e-6) of a .5
+    tie; the scales agree to 3 fp32 roundings."""
+    x = (WL.qproj(M=512, with_w=False) if cfg == "qproj" else WL.downproj(M=192, with_w=False))["X"]
+    z = O.rotate(x, block)
+    d64, d32 = O.quant_sym_rows(z, block), O.quant_sym_rows(z, block, "f32")
+    diff = d64["codes"] != d32["codes"]
+    assert np.all(np.abs(d64["t"] - d32["t"]) <= np.abs(d64["t"]) * SYM_T_BUDGET)
+    assert np.all(_dist_to_tie(d64["t"][diff]) <= np.abs(d64["t"][diff]) * SYM_T_BUDGET)
+    assert np.all(np.abs(d64["codes"].astype(int) - d32["codes"])[diff] == 1)
+    assert np.all(np.abs(d32["scale"] - d64["scale"]) <= 3.001 * 2.0 ** -24 * d64["scale"])
+
+
+def test_decision_modes_agree_off_ties_asym():
+    x = WL.gateup(M=96, with_w=False)["X"]
+    z = O.rotate(x, 128)
+    d64, d32 = O.quant_asym_groups(z, 128), O.quant_asym_groups(z, 128, mode="f32")
+    assert np.all(np.abs(d64["t"] - d32["t"]) <= np.abs(d64["t"]) * ASYM_T_BUDGET)
+    assert np.all(np.abs(d64["t_zp"] - d32["t_zp"]) <= np.abs(d64["t_zp"]) * ASYM_T_BUDGET)
+    zdiff = d64["zp"] != d32["zp"]
+    assert np.all(_dist_to_tie(d64["t_zp"][zdiff]) <= np.abs(d64["t_zp"][zdiff]) * ASYM_T_BUDGET)
+    lv64 = d64["codes"].astype(int).reshape(96, 64, 128) - d64["zp"][:, :, None]
+    lv32 = d32["codes"].astype(int).reshape(96, 64, 128) - d32["zp"][:, :, None]
+    diff = (lv64 != lv32).reshape(96, -1)
+    near = _dist_to_tie(d64["t"]) <= np.abs(d64["t"]) * ASYM_T_BUDGET
+    near |= np.repeat(zdiff, 128, axis=1)
+    assert np.all(near[diff])
+
+
+def test_decision_modes_agree_off_ties_mx():
+    """MXFP4: y32 = fl32(fl32(z) * fl32(1/sqrt(b))) is within 3 fp32 roundings
+    of z / sqrt(b); exponents differ only where the block maximum is that close
+    to a power of two, codes only that close to an E2M1 midpoint."""
+    x = WL.qproj(M=256, with_w=False)["X"]
+    for block in (128, 4096):
+        d64, d32 = O.rotate_mx_quant(x, block), O.rotate_mx_quant(x, block, decide="f32")
+        assert np.all(np.abs(d64["y"] - d32["y"]) <= np.abs(d64["y"]) * SYM_T_BUDGET)
+        ediff = d64["scale_e"] != d32["scale_e"]
+        amax = np.abs(d64["y"].reshape(256, -1, 32)).max(axis=-1)
+        lg = np.log2(amax)
+        assert np.all(np.abs(lg - np.round(lg))[ediff] <= 2 * SYM_T_BUDGET)
+        t = d64["y"].reshape(256, -1, 32) / np.exp2(d64["scale_e"])[..., None]
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        near = (np.abs(np.abs(t)[..., None] - mids) <= mids * SYM_T_BUDGET).any(axis=-1)
+        near |= np.repeat(ediff[..., None], 32, axis=-1)
+        cdiff = (d64["codes"] != d32["codes"]).reshape(near.shape)
+        assert np.all(near[cdiff])
 
 
 @pytest.mark.parametrize("block", [128, 4096])
@@ -453,10 +545,13 @@ def test_signed_outlier_codes_closed_form(n, j):
     x = np.zeros((1, n))
     x[0, j] = m
     d = WL.hadamard_signs(n, seed=j)
-    q = O.rotate_quant_act(x, n, "sym", signs=d)
     expect = np.array([7 * int(d[j]) * (-1) ** bin(i & j).count("1") for i in range(n)])
-    assert np.array_equal(q["codes"][0], expect)
+    for decide in ("f64", "f32"):
+        q = O.rotate_quant_act(x, n, "sym", signs=d, decide=decide)
+        assert np.array_equal(q["codes"][0], expect)
     assert q["scale"][0] == np.float32(np.float32(m) / np.float32(7.0 * math.sqrt(n)))
+    assert math.isclose(O.rotate_quant_act(x, n, "sym", signs=d)["scale"][0], m / (7.0 * math.sqrt(n)),
+                        rel_tol=4e-16)
 
 
 def test_signed_rotation_lowers_int4_product_error():
