@@ -340,6 +340,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first; a few hundred let the clocks settle")
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="keep running untimed steps until this much wall time has passed, "
+                         "whatever --warmup says, so that short runs still time settled clocks")
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
@@ -410,10 +413,18 @@ def main() -> int:
         if st:
             raise RuntimeError(f"W4A4 call failed: {_lib.last_error()}")
 
-    for i in range(args.warmup):
+    # untimed warm-up: --warmup steps, extended to --min-warmup-s seconds of
+    # device work (the GPU clocks take a few hundred steps to settle)
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         s = ptrs[i % NSETS]
         check(weight(s) | act(s) | gemm(s))
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup_done = i
 
     # The GEMM launch of every timed step carries its own pair of events: the
     # runtime stamps the kernel's start and end into them (no marker packets
@@ -464,6 +475,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_done,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -475,7 +487,7 @@ def main() -> int:
                    "M": M, "N": N, "K": K, "had_block": block},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic, "kernel": "w4a4_gemm (gemm_adirect_kernel, 256x128 tiles)",
+                     "traffic": traffic, "kernel": "w4a4_gemm (gemm_adirect_kernel<8, 2, 4>, 256x128 tiles)",
                      "per_launch_ops": ops, "avg_launch_ms": round(kt["w4a4_gemm"], 5)},
         "kernels": {
             "w4a4_gemm": {"avg_ms": round(kt["w4a4_gemm"], 5), "TOPS": round(gemm_tops, 1),

@@ -17,6 +17,12 @@
 // Asymmetric activations (unsigned codes, one zero-point per row and group of
 // 128) are widened to the exact levels u - zp in [-15, 15], so the weights'
 // 16x factor leaves 16 * A_g in the accumulator.
+//
+// Operand order: the prefill kernels pass the weight fragment as the MFMA's
+// first operand and the activation fragment as its second, so each lane of
+// a 16x16 output block ends up with one output row and four consecutive
+// columns (16 contiguous bytes of Y): the epilogue stores them with one
+// DPP exchange per value instead of a 4x4 transpose.
 #include "common.h"
 #include "kernels.h"
 #include "tile.h"
@@ -61,11 +67,11 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles_m = (p.M + BMD - 1) / BMD;
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BMD, n0 = tn * BN;
   const int nkt = p.K / BK;
   const int64_t ldc = p.K / 2;
@@ -140,7 +146,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
       for (int j = 0; j < 8; ++j) {
         const v4i b = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + (h ? bf1 : bf0));
 #pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][j] = mfma16(a[i][h], b, acc[i][j]);
+        for (int i = 0; i < TM; ++i) acc[i][j] = mfma16(b, a[i][h], acc[i][j]);
       }
     }
   };
@@ -166,27 +172,31 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
   }
   if (nkt & 1) compute(pa0, 0);
 
-  // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
-  // block; after dequantizing, pairs of blocks are stored as full 128-byte
-  // row segments.
+  // epilogue: lane (fr, g) holds Y[m0 + wave*16*TM + 16 i + fr][n0 + 16 j +
+  // 4 g + v] of block (i, j); scales come through range-checked buffer
+  // loads (rows past M and columns past N read as 0 and are not stored)
+  const int64_t mw = m0 + wave * 16 * TM;
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + n0), (short)0, (int)((p.N - n0) * 4 < 0x7fffffff ? (p.N - n0) * 4 : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xs + m0), (short)0, (int)((p.M - m0) * 4 < 0x7fffffff ? (p.M - m0) * 4 : 0x7fffffff), 0x00020000);
+  const bool ld_ok = (p.ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t rb = m0 + wave * 16 * TM + 16 * i + 4 * g;
-    float sx[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sx[v] = (rb + v < p.M) ? p.xs[rb + v] : 0.0f;
+    const float sx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (wave * 16 * TM + 16 * i + fr), 0, 0));
+    const int64_t r0 = mw + 16 * i;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const int64_t col = n0 + 16 * j + fr;
-      const float sw0 = col < p.N ? p.ws[col] : 0.0f;
-      const float sw1 = col + 16 < p.N ? p.ws[col + 16] : 0.0f;
-      float y0[4], y1[4];
+      const v4f swa = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 4 * g), 0, 0));
+      const v4f swb = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 16 + 4 * g), 0, 0));
+      v4f ya, yb;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        y0[v] = (sx[v] * sw0) * (float)(acc[i][j][v] >> 8);
-        y1[v] = (sx[v] * sw1) * (float)(acc[i][j + 1][v] >> 8);
+        ya[v] = (sx * swa[v]) * (float)(acc[i][j][v] >> 8);
+        yb[v] = (sx * swb[v]) * (float)(acc[i][j + 1][v] >> 8);
       }
-      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
+      const bool full = ld_ok && r0 + 16 <= p.M && n0 + 16 * j + 32 <= p.N;
+      store_pair_rows(p.y, p.ldy, p.M, p.N, r0, n0 + 16 * j, fr, g, full, ya, yb);
     }
   }
 }
@@ -197,8 +207,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
 // each wave widens its A rows straight to the int8 levels u - zp (|u - zp| <=
 // 15), so the MFMA accumulates 16 * A_g exactly; every group's sum is folded
 // into fp32 with that row's scale (block by block, inside the next group's
-// MFMA loop), and the epilogue removes the factor 16 (exact) together with
-// the weight scale.
+// MFMA sequence), and the epilogue removes the factor 16 (exact) together
+// with the weight scale.  With the weight fragment first, the activation row
+// a lane widens is also the output row it accumulates, so one zero-point
+// and one scale per row block and group serve each lane.
 template <int NW, int TM, int WPE>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmParams p) {
@@ -211,11 +223,11 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles_m = (p.M + BMD - 1) / BMD;
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BMD, n0 = tn * BN;
   const int nkt = p.K / BK;
   const int G = nkt;
@@ -243,32 +255,25 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
     b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
   }
   const int bf0 = lds_chunk(fr, 2 * g), bf1 = lds_chunk(fr, 2 * g + 1);
-
-  // per-lane row bookkeeping, relative to m0: the A row a lane widens
-  // (zero-point) and the four C rows it accumulates (scales)
-  int arow[TM], crow[TM];
+  // the activation row a lane widens and accumulates, as an offset into [rows][G]
+  int arow[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    arow[i] = wave * 16 * TM + 16 * i + fr;
-    crow[i] = wave * 16 * TM + 16 * i + 4 * g;
-  }
+  for (int i = 0; i < TM; ++i) arow[i] = (wave * 16 * TM + 16 * i + fr) * G;
 
-  // A codes, zero-points and the C rows' scales of a K step travel together,
-  // loaded one group ahead of their use (right after the step before it);
-  // all are buffer loads (no branches, so no wait is forced until the step
-  // that consumes them)
+  // A codes, zero-points and scales of a group travel together, loaded one
+  // group ahead of their use (right after the step before it); all are
+  // buffer loads (no branches, so no wait is forced until the step that
+  // consumes them)
   uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
   uint32_t z0[TM], z1[TM];
-  float s0[TM][4], s1[TM][4];
-  auto load_a = [&](uint4* pa, uint32_t* z, float (*sx)[4], int kt) {
+  float s0[TM], s1[TM];
+  auto load_a = [&](uint4* pa, uint32_t* z, float* sx, int kt) {
     const int kc = kt < nkt ? kt : nkt - 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
-      z[i] = __builtin_amdgcn_raw_buffer_load_b8(rz, arow[i] * G + kc, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        sx[i][v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((crow[i] + v) * G + kc), 0, 0));
+      z[i] = __builtin_amdgcn_raw_buffer_load_b8(rz, arow[i] + kc, 0, 0);
+      sx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (arow[i] + kc), 0, 0));
     }
   };
   auto load_b = [&](uint4* pb, int kt) {
@@ -292,8 +297,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   };
 
   // One accumulator set: during group g's step, block (i, j)'s group g-1
-  // result is folded into fp32 right before group g's MFMAs overwrite it, so
-  // the fold's VALU work interleaves with the MFMAs inside every wave.
+  // result is folded into fp32 right before group g's MFMAs overwrite it.
   // Before the first group the accumulators and the scales are zero, so that
   // first fold adds exactly 0.
   v4i acc[TM][8];
@@ -306,53 +310,77 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 #pragma unroll
       for (int v = 0; v < 4; ++v) yf[i][j][v] = 0.0f;
     }
-  auto step = [&](const uint4* pa, const uint32_t* z, const float (*sprev)[4], int stage) {
-    v4i a[TM][2];
+  // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
+  auto widen_row = [&](const uint4& pa, uint32_t z, v4i& a0, v4i& a1) {
+    const uint32_t bias = (128u - z) * 0x01010101u;
+    const uint32_t w[4] = {pa.x, pa.y, pa.z, pa.w};
+    uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
-      const uint32_t bias = (128u - z[i]) * 0x01010101u;
-      const uint32_t w[4] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        o[2 * d] = ((w[d] & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
-        o[2 * d + 1] = (((w[d] >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
-      }
-      a[i][0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-      a[i][1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+    for (int d = 0; d < 4; ++d) {
+      o[2 * d] = ((w[d] & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+      o[2 * d + 1] = (((w[d] >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
     }
+    a0 = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    a1 = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+  };
+  auto fold = [&](int i, int j, float sp) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sp, (float)acc[i][j][v], yf[i][j][v]);
+  };
+  // One group: B fragments are read two block columns ahead, and in every
+  // block column the fold of each row block sits between MFMAs (the second
+  // MFMA of a block's chain comes after the first MFMA of the other row
+  // blocks).  sched_barrier fences pin that order: left to itself the
+  // compiler hoists every fold above the first MFMA of the group (the waves
+  // of a SIMD then run VALU-only and MFMA-only phases in lockstep) and
+  // spills; pinned, the group runs 3-10% faster with 202 VGPRs.
+  auto step = [&](const uint4* pa, const uint32_t* z, const float* sprev, int stage) {
     const uint8_t* Bs = smem + stage * BSTAGE;
+    v4i bq0[3], bq1[3];
+    bq0[0] = *reinterpret_cast<const v4i*>(Bs + bf0);
+    bq1[0] = *reinterpret_cast<const v4i*>(Bs + bf1);
+    bq0[1] = *reinterpret_cast<const v4i*>(Bs + 16 * LROW + bf0);
+    bq1[1] = *reinterpret_cast<const v4i*>(Bs + 16 * LROW + bf1);
+    v4i a[TM][2];
+    widen_row(pa[0], z[0], a[0][0], a[0][1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const v4i b0 = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + bf0);
-      const v4i b1 = *reinterpret_cast<const v4i*>(Bs + j * 16 * LROW + bf1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sprev[i][v], (float)acc[i][j][v], yf[i][j][v]);
-        acc[i][j] = mfma16(a[i][1], b1, mfma16(a[i][0], b0, v4i{0, 0, 0, 0}));
+      const v4i b0 = bq0[j % 3], b1 = bq1[j % 3];
+      if (j + 2 < 8) {
+        bq0[(j + 2) % 3] = *reinterpret_cast<const v4i*>(Bs + (j + 2) * 16 * LROW + bf0);
+        bq1[(j + 2) % 3] = *reinterpret_cast<const v4i*>(Bs + (j + 2) * 16 * LROW + bf1);
       }
+      fold(0, j, sprev[0]);
+      v4i t[TM];
+      t[0] = mfma16(b0, a[0][0], v4i{0, 0, 0, 0});
+      if (j == 0) {
+#pragma unroll
+        for (int i = 1; i < TM; ++i) widen_row(pa[i], z[i], a[i][0], a[i][1]);
+      }
+#pragma unroll
+      for (int i = 1; i < TM; ++i) {
+        fold(i, j, sprev[i]);
+        t[i] = mfma16(b0, a[i][0], v4i{0, 0, 0, 0});
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i][j] = mfma16(b1, a[i][1], t[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto fold_all = [&](const float (*sf)[4]) {
+  auto fold_all = [&](const float* sf) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sf[i][v], (float)acc[i][j][v], yf[i][j][v]);
+      for (int j = 0; j < 8; ++j) fold(i, j, sf[i]);
   };
 
-  // Group g's codes and zero-points sit in register set g & 1 and its scales
-  // in set g & 1 too; group g's step folds group g-1 with the scales of set
-  // (g-1) & 1, which is refilled right afterwards with group g+1's codes,
-  // zero-points and scales (one group ahead).  Set 1 starts with zero scales.
+  // Group g's codes, zero-points and scales sit in register set g & 1; group
+  // g's step folds group g-1 with the scales of set (g-1) & 1, which is
+  // refilled right afterwards with group g+1's data (one group ahead).  Set
+  // 1 starts with zero scales.
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s1[i][v] = 0.0f;
-  }
+  for (int i = 0; i < TM; ++i) s1[i] = 0.0f;
   load_a(pa0, z0, s0, 0);
   load_b(pb0, 0);
   load_b(pb1, 1);
@@ -379,21 +407,25 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 
   // the accumulators hold 16 x the levels' products: the exact power-of-two
   // factor is removed here, once, with the weight scale
+  const int64_t mw = m0 + wave * 16 * TM;
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + n0), (short)0, (int)((p.N - n0) * 4 < 0x7fffffff ? (p.N - n0) * 4 : 0x7fffffff), 0x00020000);
+  const bool ld_ok = (p.ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t rb = m0 + crow[i];
+    const int64_t r0 = mw + 16 * i;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const int64_t col = n0 + 16 * j + fr;
-      const float sw0 = col < p.N ? p.ws[col] * 0.0625f : 0.0f;
-      const float sw1 = col + 16 < p.N ? p.ws[col + 16] * 0.0625f : 0.0f;
-      float y0[4], y1[4];
+      const v4f swa = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 4 * g), 0, 0));
+      const v4f swb = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 16 + 4 * g), 0, 0));
+      v4f ya, yb;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        y0[v] = yf[i][j][v] * sw0;
-        y1[v] = yf[i][j + 1][v] * sw1;
+        ya[v] = yf[i][j][v] * (swa[v] * 0.0625f);
+        yb[v] = yf[i][j + 1][v] * (swb[v] * 0.0625f);
       }
-      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
+      const bool full = ld_ok && r0 + 16 <= p.M && n0 + 16 * j + 32 <= p.N;
+      store_pair_rows(p.y, p.ldy, p.M, p.N, r0, n0 + 16 * j, fr, g, full, ya, yb);
     }
   }
 }

@@ -15,8 +15,11 @@
 // Lane layout of one 16x16x128 product (lane l = 16 g + r): A row r and
 // B row r, K elements 32 g .. 32 g + 31 (packed bytes 16 g .. 16 g + 15 of
 // the 64-byte step), exponent of (row r, block g); C rows 4 g .. 4 g + 3 of
-// column r.  The packed operands keep the INT4 kernels' tiling: A rows
-// straight from global memory into registers, B rows staged through LDS.
+// column r.  The prefill kernel passes the weight fragment first and the
+// activation fragment second, so C's rows are output columns: lane (r, g)
+// holds output row r, columns 4 g .. 4 g + 3 (16 contiguous bytes).  The
+// packed operands keep the INT4 kernels' tiling: A rows straight from
+// global memory into registers, B rows staged through LDS.
 //
 // Exponent bytes: a row holds 4 per 128-wide K step, [4 kt + g].  A lane
 // loads the 16 bytes of four steps of its row at once and gathers the 4
@@ -33,7 +36,6 @@ namespace w4a4 {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 128;       // output columns per workgroup
 constexpr int kKS = 128;       // K elements per step (64 packed bytes of a row)
@@ -104,7 +106,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tiles_n = (p.N + kBN - 1) / kBN;
   const int64_t tiles_m = (p.M + BMD - 1) / BMD;
   int64_t tm, tn;
@@ -182,7 +184,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
     for (int j = 0; j < 8; ++j) {
       const uint4 b = *reinterpret_cast<const uint4*>(Bs + j * 16 * kRow + bf);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][j] = mfma_mx<S>(pa[i], ae[i], b, be[j], acc[i][j]);
+      for (int i = 0; i < TM; ++i) acc[i][j] = mfma_mx<S>(b, be[j], pa[i], ae[i], acc[i][j]);
     }
   };
   using S0 = std::integral_constant<int, 0>;
@@ -228,16 +230,16 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
     __syncthreads();
   }
 
-  // epilogue: lane (fr, g) holds rows 4g..4g+3 of column fr of every 16x16
-  // block; pairs of blocks are stored as full 128-byte row segments.
+  // epilogue: lane (fr, g) holds Y[m0 + wave*16*TM + 16 i + fr][n0 + 16 j +
+  // 4 g + v] of block (i, j); pairs of blocks go out as full 128-byte rows
+  const bool ld_ok = (p.ldy & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t rb = m0 + wave * 16 * TM + 16 * i + 4 * g;
+    const int64_t r0 = m0 + wave * 16 * TM + 16 * i;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      float y0[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      float y1[4] = {acc[i][j + 1][0], acc[i][j + 1][1], acc[i][j + 1][2], acc[i][j + 1][3]};
-      store_block_pair(p.y, p.ldy, p.M, p.N, rb, n0 + 16 * j, fr, y0, y1);
+      const bool full = ld_ok && r0 + 16 <= p.M && n0 + 16 * j + 32 <= p.N;
+      store_pair_rows(p.y, p.ldy, p.M, p.N, r0, n0 + 16 * j, fr, g, full, acc[i][j], acc[i][j + 1]);
     }
   }
 }

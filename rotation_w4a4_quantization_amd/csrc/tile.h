@@ -38,82 +38,69 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn = r / gsz;
 }
 
-// 16-byte output store marked non-temporal: the fp32 result is written once
-// and not re-read by this kernel, so it should not displace the operand rows
-// that other tiles still read from L2 / MALL (measured 3-15% faster).
-__device__ __forceinline__ void store_stream4(float* dst, const float* y) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(v4f{y[0], y[1], y[2], y[3]}, reinterpret_cast<v4f*>(dst));
+// XCD-aware tile coordinates.  Workgroup i of a launch runs on XCD i % 8 of
+// the 8 that share the chip, and each XCD has its own L2.  The first
+// 8 * floor(T / 8) workgroups are renumbered so that XCD x receives the
+// contiguous range [x T8/8, (x + 1) T8/8) of a grouped order with groups of
+// 4 tile rows, i.e. compact blocks of tiles whose A and B rows its L2 shares
+// (measured on the q_proj and 8192 x 4096 x 4096 shapes: 2-4% faster than
+// the 16-row grouped order with no renumbering).  The remaining T % 8
+// workgroups keep their own index.  The mapping is a bijection of [0, T).
+__device__ __forceinline__ void tile_coords_xcd(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  constexpr int64_t GM = 4;
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t T8 = T - T % 8;
+  int64_t pid = blockIdx.x;
+  if (pid < T8) pid = (pid % 8) * (T8 / 8) + pid / 8;
+  const int64_t in_group = GM * tiles_n;
+  const int64_t gid = pid / in_group;
+  const int64_t first_m = gid * GM;
+  const int64_t gsz = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+  const int64_t r = pid - gid * in_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
 }
 
-// 4x4 transpose inside a quad of lanes: on entry lane k of the quad holds
-// column k of a 4x4 block in y[0..3] (y[v] = row v); on exit it holds row k
-// (y[c] = column c).  Two butterflies swap a lane-index bit with a
-// register-index bit (DPP quad permutes).
-__device__ __forceinline__ void quad_transpose4(float* y, int k) {
-  {
-    const bool hi = k & 1;
-#pragma unroll
-    for (int m = 0; m < 4; m += 2) {
-      const float send = hi ? y[m] : y[m + 1];
-      const float recv = dpp_f<0xB1>(send);
-      y[m] = hi ? recv : y[m];
-      y[m + 1] = hi ? y[m + 1] : recv;
-    }
-  }
-  {
-    const bool hi = k & 2;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const float send = hi ? y[m] : y[m + 2];
-      const float recv = dpp_f<0x4E>(send);
-      y[m] = hi ? recv : y[m];
-      y[m + 2] = hi ? y[m + 2] : recv;
-    }
-  }
-}
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Stores two horizontally adjacent 16x16 fp32 output blocks as full 128-byte
-// row segments.  On entry lane (fr, g) = (lane & 15, lane >> 4) holds rows
-// 4g..4g+3 of column fr of the left block in y0[0..3] and of the right block
-// in y1[0..3] (the MFMA output layout); `rb` is the output row of y*[0] and
-// `cb` the first column of the left block.  After a quad transpose of each
-// block, lane k of a quad holds 4 consecutive columns of row rb + k; lanes k
-// and k ^ 2 then trade halves, so that each of the two 16-byte stores per
-// lane writes 8 rows x 32 consecutive columns: 8 lanes cover each 128-byte
-// row segment, instead of 16 rows x 64 bytes (measured on the q_proj GEMM:
-// the 32 MiB output phase drops from about 7 to 5.5 us).  Rows at or past M
-// and columns at or past N are not written.
-__device__ __forceinline__ void store_block_pair(float* y, int64_t ldy, int64_t M, int64_t N,
-                                                 int64_t rb, int64_t cb, int fr, float* y0, float* y1) {
-  const int k = fr & 3;
-  quad_transpose4(y0, k);
-  quad_transpose4(y1, k);
-  const bool hi = k & 2;
-  float first[4], second[4];
+// Stores two horizontally adjacent 16x16 fp32 output blocks held in the
+// layout of an MFMA whose first operand is the weight fragment and second
+// the activation fragment: lane (fr, g) = (lane & 15, lane >> 4) holds row
+// r0 + fr, columns c0 + 4g .. c0 + 4g + 3 of the left block in ya and of
+// the right block (columns + 16) in yb.  In the fast path (`full`: the
+// 16 x 32 region lies inside M x N and ldy is a multiple of 4 floats) lanes
+// fr and fr ^ 8 trade one block (one DPP row rotate by 8 per value), so that
+// each of the two 16-byte non-temporal stores per lane writes 8 rows x 128
+// contiguous bytes: full cache lines (the 32 MiB q_proj output phase drops
+// from about 7 to 5.5 us against 64-byte row segments).  Otherwise every
+// element is stored under its own row and column check.  The output is not
+// re-read, so the stores bypass the caches' retention (measured 3-15%
+// faster).
+__device__ __forceinline__ void store_pair_rows(float* y, int64_t ldy, int64_t M, int64_t N, int64_t r0,
+                                                int64_t c0, int fr, int g, bool full, v4f ya, v4f yb) {
+  if (full) {
+    const bool lo = fr < 8;
+    v4f out1, out2;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float recv = dpp_f<0x4E>(hi ? y0[c] : y1[c]);   // from lane k ^ 2
-    first[c] = hi ? recv : y0[c];
-    second[c] = hi ? y1[c] : recv;
-  }
-  // first: row rb + (k & 1) of the left block (k < 2) or of the right block
-  // (k >= 2); second: row rb + 2 + (k & 1), same blocks
-  const int64_t r = rb + (k & 1);
-  const int64_t c0 = cb + (fr & ~3) + (hi ? 16 : 0);
-  const bool vec_ok = (ldy & 3) == 0 && c0 + 3 < N;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t row = r + 2 * h;
-    const float* v = h ? second : first;
+    for (int v = 0; v < 4; ++v) {
+      const float send = lo ? yb[v] : ya[v];
+      const float recv = bitsf((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(send), 0x128, 0xF, 0xF, true));
+      out1[v] = lo ? ya[v] : recv;    // rows r0 .. r0 + 7
+      out2[v] = lo ? recv : yb[v];    // rows r0 + 8 .. r0 + 15
+    }
+    const int64_t r1 = r0 + (lo ? fr : fr - 8);
+    const int64_t c = c0 + (lo ? 0 : 16) + 4 * g;
+    __builtin_nontemporal_store(out1, reinterpret_cast<v4f*>(y + r1 * ldy + c));
+    __builtin_nontemporal_store(out2, reinterpret_cast<v4f*>(y + (r1 + 8) * ldy + c));
+  } else {
+    const int64_t row = r0 + fr;
     if (row < M) {
-      float* dst = y + row * ldy + c0;
-      if (vec_ok) {
-        store_stream4(dst, v);
-      } else {
+      const int64_t c = c0 + 4 * g;
+      float* dst = y + row * ldy + c;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (c0 + c < N) dst[c] = v[c];
+      for (int v = 0; v < 4; ++v) {
+        if (c + v < N) dst[v] = ya[v];
+        if (c + 16 + v < N) dst[16 + v] = yb[v];
       }
     }
   }
