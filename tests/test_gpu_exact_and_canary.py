@@ -17,7 +17,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from parity import check_asym, check_mx, check_sym, rel_fro
+from parity import check_asym, check_gsum, check_mx, check_sym, rel_fro
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -165,9 +165,9 @@ def test_quant_weight_offline_writes_nothing_past_its_outputs():
     assert st == 0, _lib.last_error()
     assert _tail_ok(c, nc) and _tail_ok(s, ns) and _tail_ok(g, ng)
     codes = host(c[:nc]).reshape(N, K // 2)
-    check_sym(codes, host(s[:ns]).view(np.float32), O.quant_weight_offline(w, 128))
-    assert np.array_equal(host(g[:ng]).view(np.int32).reshape(N, -1),
-                          O.group_sums(O.unpack_nibbles(codes, signed=True)))
+    ref = O.quant_weight_offline(w, 128)
+    check_sym(codes, host(s[:ns]).view(np.float32), ref)
+    check_gsum(host(g[:ng]).view(np.int32).reshape(N, -1), codes, ref)
 
 
 def test_rotate_quant_mxfp4_writes_nothing_past_its_outputs():

@@ -16,7 +16,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from parity import Y_RTOL_FRO, check_mx, rel_fro
+from parity import Y_RTOL_FRO, check_mx, decode_nibbles, rel_fro
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -41,7 +41,15 @@ def gpu_mx(x, block, signs=None):
 
 
 def mx_codes(packed):
+    """Codes of an oracle-packed operand (inputs made on the test side)."""
     return O.unpack_nibbles(packed, signed=False)
+
+
+def _same_mx(packed_gpu, sbytes_gpu, ref):
+    """Rows whose GPU codes and exponents equal the oracle's."""
+    c = decode_nibbles(packed_gpu, signed=False) == ref["codes"]
+    e = (np.asarray(sbytes_gpu, np.int64) - 127) == ref["scale_e"]
+    return np.all(c, axis=1) & np.all(e, axis=1)
 
 
 def abs_terms(cx, ex, cw, ew):
@@ -159,14 +167,21 @@ def test_rotate_quant_mxfp4_stride_and_empty():
 
 
 @pytest.mark.parametrize("cfg,block", [("qproj", 128), ("qproj", 4096), ("downproj", 128)])
-def test_rotate_quant_mxfp4_full_size_sampled(cfg, block):
-    """Full-size launch; rows are independent, so a seeded sample of rows is
-    checked against the oracle."""
+def test_rotate_quant_mxfp4_full_size(cfg, block):
+    """Full-size launch; every q_proj row, and 1024 seeded down_proj rows in
+    chunks (rows are independent), checked against the oracle."""
     x = WL.qproj(with_w=False)["X"] if cfg == "qproj" else WL.downproj(with_w=False)["X"]
     c, e = gpu_mx(x, block)
-    rows = np.sort(np.random.default_rng(5).choice(x.shape[0], 192, replace=False))
+    if cfg == "qproj":
+        rows = np.arange(x.shape[0])
+    else:
+        rows = np.sort(np.random.default_rng(5).choice(x.shape[0], 1024, replace=False))
     b = 128 if block == 128 else x.shape[1]
-    print(cfg, block, check_mx(c[rows], e[rows], O.rotate_mx_quant(x[rows], b)))
+    flips = 0
+    for k in range(0, len(rows), 256):
+        r = rows[k:k + 256]
+        flips += check_mx(c[r], e[r], O.rotate_mx_quant(x[r], b))["flips"]
+    print(cfg, block, "rows", len(rows), "flips", flips)
 
 
 # ---------------------------------------------------------------- MXFP4 GEMM
@@ -253,10 +268,13 @@ def test_mxfp4_linear_end_to_end(cfg):
     cx, ex = R.rotate_quant_mxfp4(dev(X), 128)
     cw, ew = R.rotate_quant_mxfp4(dev(W), 128)
     y = host(R.mxfp4_gemm(cx, ex, cw, ew))[np.ix_(rows, cols)]
-    hcx, hex_ = host(cx)[rows], host(ex)[rows].astype(np.int64) - 127
-    hcw, hew = host(cw)[cols], host(ew)[cols].astype(np.int64) - 127
-    check_product(y, mx_codes(hcx), hex_, mx_codes(hcw), hew)
     ax, aw = O.rotate_mx_quant(X[rows], 128), O.rotate_mx_quant(W[cols], 128)
+    # rows and columns whose GPU codes and exponents equal the oracle's: the
+    # product there is the oracle's product of its own codes to the fp32 bound
+    rx = _same_mx(host(cx)[rows], host(ex)[rows], ax)
+    rw = _same_mx(host(cw)[cols], host(ew)[cols], aw)
+    assert rx.mean() > 0.9 and rw.mean() > 0.9
+    check_product(y[np.ix_(rx, rw)], ax["codes"][rx], ax["scale_e"][rx], aw["codes"][rw], aw["scale_e"][rw])
     ref = O.mx_gemm_f64(ax["codes"], ax["scale_e"], aw["codes"], aw["scale_e"])
     r = rel_fro(y, ref)
     exact = np.asarray(X[rows], np.float64) @ np.asarray(W[cols], np.float64).T

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from parity import Y_RTOL_FRO, check_asym, check_sym, rel_fro
+from parity import Y_RTOL_FRO, check_asym, check_gsum, check_sym, rel_fro
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -74,8 +74,9 @@ def test_signed_weight_offline(block):
     d = WL.hadamard_signs(4096, seed=11)
     c, s, g = R.quant_weight_offline(dev(w), block if block == 128 else "full", signs=dev(d))
     c, s, g = host(c), host(s), host(g)
-    check_sym(c, s, O.quant_weight_offline(w, block, signs=d))
-    assert np.array_equal(g, O.group_sums(O.unpack_nibbles(c, signed=True)))
+    ref = O.quant_weight_offline(w, block, signs=d)
+    check_sym(c, s, ref)
+    check_gsum(g, c, ref)
 
 
 def test_signed_kv_dense_and_strided():
