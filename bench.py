@@ -257,6 +257,25 @@ def run_suite(torch, R, WL):
     emit("kv4_attention_decode", "q 8x32 over kv 8x32x4096x128 int4",
          _time_kernel(torch, lambda: R.kv4_attention_decode(q, kc, ks, kz, vc, vs, vz, out=o), flush),
          nbytes=attn_bytes(8, 32, 4096))
+    del kc, vc
+    # few heads, long caches: the single pass against tokens split over
+    # workgroups (the split line times both of its kernels)
+    for B, H, S in ((1, 32, 4096), (1, 8, 32768)):
+        src = kv.reshape(-1)[:B * H * S * 128].reshape(B, H, S, 128)
+        kc, ks, kz = R.kv_rotate_quant4(src)
+        vc, vs, vz = R.kv_rotate_quant4(src.flip(1).contiguous())
+        q = T(WL.small_random(124, B * H, 128).reshape(B, H, 128))
+        o = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(R.kv4_attention_workspace_bytes(B, H, S), 16),), dtype=torch.uint8, device=dev)
+        cfg = f"q {B}x{H} over kv {B}x{H}x{S}x128 int4"
+        emit("kv4_attention_decode", cfg,
+             _time_kernel(torch, lambda: R.kv4_attention_decode(q, kc, ks, kz, vc, vs, vz, out=o), flush),
+             nbytes=attn_bytes(B, H, S))
+        emit("kv4_attention_decode_ws", cfg,
+             _time_kernel(torch, lambda: R.kv4_attention_decode_split(q, kc, ks, kz, vc, vs, vz, out=o,
+                                                                      workspace=ws), flush),
+             nbytes=attn_bytes(B, H, S))
+        del kc, vc, src
 
 
 def attn_bytes(B: int, H: int, S: int) -> int:
@@ -317,6 +336,10 @@ def run_only(torch, R, WL, which, steps, had):
         xc, xs, xz = R.rotate_quant_act(x, 128, "asym")
         y = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
         fn = lambda: R.w4a4_gemm(xc, xs, xz, wc, ws, act_mode="asym", out=y)   # noqa: E731
+    elif which in ("downact", "gateact"):
+        x = T((WL.downproj(with_w=False) if which == "downact" else WL.gateup(with_w=False))["X"])
+        mode = "sym" if which == "downact" else "asym"
+        fn = lambda: R.rotate_quant_act(x, 128, mode)                         # noqa: E731
     elif which == "attn":
         kv = T(WL.kv()["KV"])
         kc, ks, kz = R.kv_rotate_quant4(kv)
@@ -325,6 +348,16 @@ def run_only(torch, R, WL, which, steps, had):
         q = T(WL.small_random(123, 8 * 32, 128).reshape(8, 32, 128))
         o = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
         fn = lambda: R.kv4_attention_decode(q, kc, ks, kz, vc, vs, vz, out=o)  # noqa: E731
+    elif which == "attnsplit":
+        # 1 x 8 heads x 32768 tokens: tokens split over workgroups
+        kv = T(WL.kv()["KV"]).reshape(-1)[:8 * 32768 * 128].reshape(1, 8, 32768, 128)
+        kc, ks, kz = R.kv_rotate_quant4(kv)
+        vc, vs, vz = R.kv_rotate_quant4(kv.flip(1).contiguous())
+        del kv
+        q = T(WL.small_random(124, 8, 128).reshape(1, 8, 128))
+        o = torch.empty((1, 8, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty((R.kv4_attention_workspace_bytes(1, 8, 32768),), dtype=torch.uint8, device=dev)
+        fn = lambda: R.kv4_attention_decode_split(q, kc, ks, kz, vc, vs, vz, out=o, workspace=ws)  # noqa: E731
     else:
         kv = T(WL.kv()["KV"])
         fn = lambda: R.kv_rotate_quant4(kv)                                    # noqa: E731
@@ -346,8 +379,8 @@ def main() -> int:
     ap.add_argument("--had", choices=["128", "full"], default="128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="per-kernel lines for every configuration")
-    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "decode", "gateup", "downproj", "copy",
-                                       "mx", "mxact", "mxdecode", "fused"],
+    ap.add_argument("--only", choices=["gemm", "act", "weight", "kv", "attn", "attnsplit", "decode", "gateup", "downproj", "copy",
+                                       "mx", "mxact", "mxdecode", "fused", "downact", "gateact"],
                     help="launch one kernel --steps times back to back (for rocprofv3 runs)")
     args = ap.parse_args()
 

@@ -84,7 +84,7 @@ typedef enum {
 enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
 enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
 
-#define W4A4_ABI_VERSION 4
+#define W4A4_ABI_VERSION 5
 
 /*
  * had_signs (the rotate calls and w4a4_decode_fused): NULL, or a device array of K fp16
@@ -238,6 +238,46 @@ W4A4_API w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* 
                              const uint8_t* v_codes, const float* v_scales, const uint8_t* v_zeros,
                              int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
                              const uint16_t* had_signs, float* out, void* stream);
+
+/*
+ * kv4_attention_workspace_bytes - bytes of workspace kv4_attention_decode_ws
+ * needs for B*H heads of S cached tokens: 0 when it takes the single pass
+ * (enough heads to give every compute unit a workgroup), else
+ * B * H * ranges * 528 with ranges = min(64, ceil(256 / (B H)), S / 512).
+ * Returns -1 (message in w4a4_last_error) when B, H or S is out of the
+ * ranges kv4_attention_decode accepts.  Host only; enqueues nothing.
+ */
+W4A4_API int64_t kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t S);
+
+/*
+ * kv4_attention_decode_ws - kv4_attention_decode for caches with few heads:
+ * the same result (same arguments, same rules, same output), computed with
+ * the S tokens of every head split into ranges that separate workgroups
+ * take, so that B*H heads still spread over the whole GPU.  Each range
+ * leaves its online-softmax state (rotated output sum, running maximum and
+ * sum) in `workspace`; a second kernel merges a head's states (the split of
+ * the softmax sum: o = sum_r 2^(m_r - M) o_r / sum_r 2^(m_r - M) l_r),
+ * normalizes and rotates back.  Only the fp32 summation order differs from
+ * kv4_attention_decode.
+ *   Page "QuaRot (rotation-based outlier removal, W4A4KV4)", field
+ *   "Activation scheme"; page "Rotations for 4-Bit Activations: QuaRot,
+ *   SpinQuant, and Friends", section "A rotation changes nothing, and that
+ *   is the point".
+ *
+ *   workspace        device buffer owned by the caller, 16-byte aligned, of
+ *                    workspace_bytes >= kv4_attention_workspace_bytes(B, H, S)
+ *                    bytes (W4A4_ERR_SHAPE if smaller); may be NULL when that
+ *                    size is 0.  Its contents on entry do not matter; the
+ *                    call overwrites them, and calls that overlap in time
+ *                    must not share one workspace.
+ * Two kernels are enqueued on `stream` (one when the single pass is taken).
+ */
+W4A4_API w4a4_status kv4_attention_decode_ws(const uint16_t* q_f16, const uint8_t* k_codes,
+                             const float* k_scales, const uint8_t* k_zeros,
+                             const uint8_t* v_codes, const float* v_scales, const uint8_t* v_zeros,
+                             int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
+                             const uint16_t* had_signs, float* out, void* workspace,
+                             int64_t workspace_bytes, void* stream);
 
 /*
  * rotate_quant_mxfp4 - the rotate step with MXFP4 output: per row, the same

@@ -14,6 +14,7 @@ exception.  Every step of the computation runs in the library's kernels.
     y = w4a4_decode_fused(x_small, wq, ws)      # M <= 16: both steps in one launch
     kc, ks, kz = kv_rotate_quant4(kv)
     o = kv4_attention_decode(q, kc, ks, kz, vc, vs, vz)   # decode attention on the INT4 cache
+    o = kv4_attention_decode_split(q, kc, ks, kz, vc, vs, vz)   # the same, tokens split (few heads)
     # MXFP4 (E2M1 codes, a power-of-two scale per 32) on the scaled FP4 MFMA
     xc, xe = rotate_quant_mxfp4(x, had_block=128)
     wc, we = rotate_quant_mxfp4(w, had_block=128)
@@ -28,8 +29,8 @@ from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HA
                    last_error)
 
 __all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
-           "kv4_attention_decode", "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "abi_version",
-           "W4A4Error"]
+           "kv4_attention_decode", "kv4_attention_decode_split", "kv4_attention_workspace_bytes",
+           "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "abi_version", "W4A4Error"]
 
 _MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
 
@@ -227,8 +228,29 @@ def kv_rotate_quant4(kv: torch.Tensor, signs=None):
     return codes, scales, zeros
 
 
+def kv4_attention_workspace_bytes(B: int, H: int, S: int) -> int:
+    """Bytes of workspace kv4_attention_decode_split needs (0: single pass)."""
+    n = int(_lib.load().kv4_attention_workspace_bytes(B, H, S))
+    if n < 0:
+        raise ValueError(f"kv4_attention_workspace_bytes: {last_error()}")
+    return n
+
+
+def kv4_attention_decode_split(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
+                               softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None):
+    """kv4_attention_decode with each head's tokens split over workgroups
+    (kv4_attention_decode_ws): the same result for caches with few heads,
+    faster when B*H is small.  `workspace` (uint8, at least
+    kv4_attention_workspace_bytes(B, H, S) bytes) is allocated here if not
+    given."""
+    return kv4_attention_decode(q, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, softmax_scale, signs,
+                                out, _split=True, _workspace=workspace)
+
+
 def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
-                         softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None):
+                         softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None,
+                         _split: bool = False, _workspace: torch.Tensor | None = None):
     """Single-query attention per (batch, head) over a KV cache written by
     kv_rotate_quant4 (rotated asymmetric INT4); q fp16 [B, H, 128].
 
@@ -258,6 +280,20 @@ def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v
     if tuple(y.shape) != (B, H, D) or not y.is_contiguous():
         raise ValueError("out must be a contiguous [B, H, D] fp32 tensor")
     sg = _signs(signs, D, dev)
+    if _split:
+        need = kv4_attention_workspace_bytes(B, H, S) if B * H > 0 else 0
+        ws = _workspace
+        if ws is None and need > 0:
+            ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        if ws is not None:
+            _need(ws, torch.uint8, "workspace")
+            if not ws.is_contiguous() or ws.device != dev:
+                raise ValueError("workspace must be a contiguous uint8 tensor on the device of q")
+        st = _lib.call("kv4_attention_decode_ws", _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),
+                       _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), B, H, S, D, scale, _ptr(sg), _ptr(y),
+                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+        _check(st, "kv4_attention_decode_ws")
+        return y
     st = _lib.call("kv4_attention_decode", _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),
                    _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), B, H, S, D, scale, _ptr(sg), _ptr(y),
                    _stream(dev))

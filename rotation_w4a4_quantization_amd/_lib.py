@@ -31,7 +31,11 @@ SIGNATURES = {
     "rotate_quant_mxfp4": [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp],
     "w4a4_decode_fused": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "mxfp4_gemm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
+    "kv4_attention_decode_ws": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                _vp, _vp, _vp, _i64, _vp],
 }
+# entry points that return a value other than a status
+SIZE_FUNCS = {"kv4_attention_workspace_bytes": [_i64, _i64, _i64]}
 
 _lib = None
 
@@ -48,6 +52,10 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        for name, args in SIZE_FUNCS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int64
         lib.w4a4_last_error.argtypes = []
         lib.w4a4_last_error.restype = ctypes.c_char_p
         lib.w4a4_abi_version.argtypes = []

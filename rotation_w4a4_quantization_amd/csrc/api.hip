@@ -338,4 +338,48 @@ w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* k_codes, 
   return launched(w4a4::launch_kv4_attention(p, (hipStream_t)stream), "kv4_attention_decode");
 }
 
+int64_t kv4_attention_workspace_bytes(int64_t B, int64_t H, int64_t S) {
+  if (B < 0 || H < 0 || S < 1 || S >= (int64_t(1) << 25) || H >= (int64_t(1) << 31) ||
+      (B > 0 && (B >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)))) {
+    fail(W4A4_ERR_SHAPE, "B=%lld, H=%lld, S=%lld out of range", (long long)B, (long long)H, (long long)S);
+    return -1;
+  }
+  ok();
+  return w4a4v::attention_workspace_bytes(B * H, S);
+}
+
+w4a4_status kv4_attention_decode_ws(const uint16_t* q_f16, const uint8_t* k_codes, const float* k_scales,
+                                    const uint8_t* k_zeros, const uint8_t* v_codes, const float* v_scales,
+                                    const uint8_t* v_zeros, int64_t B, int64_t H, int64_t S, int64_t D,
+                                    float softmax_scale, const uint16_t* had_signs, float* out, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
+  static_assert(w4a4::kAttnPartFloats * 4 == w4a4v::kAttnPartBytes, "partial-state size");
+  TimingScope timing_scope;
+  w4a4v::Msg m;
+  bool noop = false;
+  if (w4a4_status s = w4a4v::kv4_attention_decode_ws(q_f16, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
+                                                     B, H, S, D, softmax_scale, had_signs, out, workspace,
+                                                     workspace_bytes, noop, m))
+    return verdict(s, m);
+  if (noop) return ok();
+  if (w4a4_status s = check_device()) return s;
+
+  w4a4::AttnParams p{};
+  p.q = q_f16;
+  p.k_codes = k_codes;
+  p.k_scales = k_scales;
+  p.k_zeros = k_zeros;
+  p.v_codes = v_codes;
+  p.v_scales = v_scales;
+  p.v_zeros = v_zeros;
+  p.signs = had_signs;
+  p.out = out;
+  p.BH = B * H;
+  p.S = S;
+  p.scale2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.nsplit = w4a4v::attention_splits(p.BH, S);
+  p.part = static_cast<float*>(workspace);
+  return launched(w4a4::launch_kv4_attention_split(p, (hipStream_t)stream), "kv4_attention_decode_ws");
+}
+
 }  // extern "C"

@@ -23,6 +23,13 @@
 // Every lane group keeps its own online-softmax state (running max, sum,
 // 32 output dims per lane); the groups of a wave are merged with xor
 // shuffles, the waves through LDS.
+//
+// Split path (few heads, long caches): one workgroup per (batch, head, token
+// range); each writes its merged state (the unnormalized rotated output
+// sum, the running maximum and sum) to a partial-state buffer, and a second
+// kernel merges a head's ranges (the same online-softmax merge), normalizes
+// and rotates back.  This is the textbook split of the softmax sum; only the
+// fp32 summation order differs from the single pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -73,6 +80,7 @@ __device__ __forceinline__ void fwht128_wave(float& a, float& b) {
   b *= r;
 }
 
+template <bool SPLIT>
 __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams p) {
   __shared__ float q_rot[128];
   __shared__ float part_m[kAttnWaves], part_l[kAttnWaves];
@@ -82,7 +90,8 @@ __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 2, j = lane & 3;
-  const int64_t bh = blockIdx.x;
+  const int64_t bh = SPLIT ? blockIdx.x / p.nsplit : blockIdx.x;
+  const int split = SPLIT ? (int)(blockIdx.x - bh * p.nsplit) : 0;
 
   // ---- rotate the query: q_rot = (q * d) H / sqrt(128)
   if (wave == 0) {
@@ -107,11 +116,15 @@ __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams 
   for (int i = 0; i < 32; ++i) q[i] = q_rot[32 * j + i];
   const float q_sum = q_sum_sh;
 
-  // ---- this wave's token slice
+  // ---- this wave's token slice of the workgroup's range (the whole cache
+  // in the single pass)
   const int64_t S = p.S;
-  const int64_t per_wave = (S + kAttnWaves - 1) / kAttnWaves;
-  const int64_t t_begin = wave * per_wave;
-  const int64_t t_end = t_begin + per_wave < S ? t_begin + per_wave : S;
+  const int64_t per_split = SPLIT ? (S + p.nsplit - 1) / p.nsplit : S;
+  const int64_t r_begin = split * per_split;
+  const int64_t r_end = r_begin + per_split < S ? r_begin + per_split : S;
+  const int64_t per_wave = (r_end - r_begin + kAttnWaves - 1) / kAttnWaves;
+  const int64_t t_begin = r_begin + wave * per_wave;
+  const int64_t t_end = t_begin + per_wave < r_end ? t_begin + per_wave : r_end;
 
   const int64_t head = bh * S;                   // first token row of this head
   const int64_t code_bytes = S * 64;
@@ -218,6 +231,18 @@ __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams 
       a = fmaf(part_o[k][lane], f, a);
       b = fmaf(part_o[k][lane + 64], f, b);
     }
+    if constexpr (SPLIT) {
+      // this range's state, unnormalized; an empty range leaves M = kNegBig
+      // and L = 0, which the merge weighs by 0
+      float* st = p.part + (bh * p.nsplit + split) * kAttnPartFloats;
+      st[lane] = a;
+      st[lane + 64] = b;
+      if (lane == 0) {
+        st[128] = M;
+        st[129] = L;
+      }
+      return;
+    }
     const float inv = 1.0f / L;
     a *= inv;
     b *= inv;
@@ -233,11 +258,53 @@ __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams 
   }
 }
 
+// Split path, second kernel: one wave per (batch, head) merges the
+// nsplit partial states o_k, m_k, l_k (m in log2 units):
+//   o_rot = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k,
+// then rotates back and applies the signs, as the single pass does.
+__global__ void __launch_bounds__(256) kv4_attention_merge_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= p.BH) return;                         // uniform over the wave
+  const float* st = p.part + bh * p.nsplit * kAttnPartFloats;
+  float M = kNegBig;
+  for (int k = 0; k < p.nsplit; ++k) M = fmaxf(M, st[k * kAttnPartFloats + 128]);
+  float L = 0.0f, a = 0.0f, b = 0.0f;
+  for (int k = 0; k < p.nsplit; ++k) {
+    const float* sk = st + k * kAttnPartFloats;
+    const float f = exp2f(sk[128] - M);
+    L = fmaf(sk[129], f, L);
+    a = fmaf(sk[lane], f, a);
+    b = fmaf(sk[lane + 64], f, b);
+  }
+  const float inv = 1.0f / L;
+  a *= inv;
+  b *= inv;
+  fwht128_wave(a, b);
+  if (p.signs) {
+    if (p.signs[lane] & 0x8000u) a = -a;
+    if (p.signs[lane + 64] & 0x8000u) b = -b;
+  }
+  float* op = p.out + bh * 128;
+  op[lane] = a;
+  op[lane + 64] = b;
+}
+
 }  // namespace
 
 hipError_t launch_kv4_attention(const AttnParams& p, hipStream_t st) {
   if (p.BH == 0) return hipSuccess;
-  W4A4_LAUNCH(kv4_attention_kernel, dim3((uint32_t)p.BH), dim3(kAttnThreads), 0, st, p);
+  W4A4_LAUNCH(kv4_attention_kernel<false>, dim3((uint32_t)p.BH), dim3(kAttnThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv4_attention_split(const AttnParams& p, hipStream_t st) {
+  if (p.BH == 0) return hipSuccess;
+  if (p.nsplit <= 1) return launch_kv4_attention(p, st);
+  const LaunchTiming t = take_launch_timing();
+  W4A4_LAUNCH_FIRST(t, kv4_attention_kernel<true>, dim3((uint32_t)(p.BH * p.nsplit)), dim3(kAttnThreads), 0, st, p);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  W4A4_LAUNCH_LAST(t, kv4_attention_merge_kernel, dim3((uint32_t)((p.BH + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

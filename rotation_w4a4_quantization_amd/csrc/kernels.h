@@ -95,9 +95,18 @@ struct AttnParams {
   float* out;                 // [BH][128] fp32
   int64_t BH, S;
   float scale2;               // softmax scale * log2(e)
+  float* part;                // split path: [BH][nsplit][kAttnPartFloats] partial states
+  int32_t nsplit;             // split path: token ranges per (batch, head)
 };
 
+// Split path: floats per partial state (128 rotated output sums, running
+// maximum, running sum, two pad floats so that every state is 16-byte aligned).
+constexpr int kAttnPartFloats = 132;
+
 hipError_t launch_kv4_attention(const AttnParams& p, hipStream_t st);
+// Split path: p.part (p.BH * p.nsplit partial states) and p.nsplit set; with
+// p.nsplit <= 1 the single pass.
+hipError_t launch_kv4_attention_split(const AttnParams& p, hipStream_t st);
 
 // Optional per-launch timing: events armed on this host thread are attached to
 // the next kernel launch (the runtime writes the kernel's own start and end
@@ -116,5 +125,13 @@ LaunchTiming take_launch_timing();
     hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, (uint32_t)(LDS), STREAM, t_.start, t_.stop, \
                           0u, __VA_ARGS__);                                                \
   } while (0)
+
+// For an entry point that enqueues two kernels: the armed start event goes
+// to the first launch and the stop event to the second (T is the pair taken
+// with take_launch_timing() before the first launch).
+#define W4A4_LAUNCH_FIRST(T, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                          \
+  hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, (uint32_t)(LDS), STREAM, (T).start, nullptr, 0u, __VA_ARGS__)
+#define W4A4_LAUNCH_LAST(T, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                           \
+  hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, (uint32_t)(LDS), STREAM, nullptr, (T).stop, 0u, __VA_ARGS__)
 
 }  // namespace w4a4

@@ -208,6 +208,47 @@ inline w4a4_status kv4_attention_decode(const void* q_f16, const void* k_codes, 
   return W4A4_OK;
 }
 
+// Token ranges per (batch, head) of the split attention path: enough for
+// about 256 workgroups (one per CU), each range at least 512 tokens (64 per
+// wave of 8), at most 64; 1 means the single pass.  Measured cold on
+// MI355X with the KV workload's value distribution: 1 x 8 heads x 32768
+// tokens 230 -> 49 us, 1 x 32 x 4096 43 -> 28 us; with 8 x 32 heads (256
+// workgroups already) one range per head is the fastest.
+inline int32_t attention_splits(int64_t BH, int64_t S) {
+  if (BH <= 0 || S <= 0) return 1;
+  int64_t ns = (256 + BH - 1) / BH;
+  const int64_t by_len = S / 512;
+  if (ns > by_len) ns = by_len;
+  if (ns > 64) ns = 64;
+  return ns < 2 ? 1 : (int32_t)ns;
+}
+
+// Bytes of partial states the split path needs (0: single pass): one state
+// of 132 floats per (batch, head, range).
+constexpr int64_t kAttnPartBytes = 132 * 4;
+inline int64_t attention_workspace_bytes(int64_t BH, int64_t S) {
+  const int32_t ns = attention_splits(BH, S);
+  return ns > 1 ? BH * ns * kAttnPartBytes : 0;
+}
+
+inline w4a4_status kv4_attention_decode_ws(const void* q_f16, const void* k_codes, const void* k_scales,
+                                           const void* k_zeros, const void* v_codes, const void* v_scales,
+                                           const void* v_zeros, int64_t B, int64_t H, int64_t S, int64_t D,
+                                           float softmax_scale, const void* had_signs, const void* out,
+                                           const void* workspace, int64_t workspace_bytes, bool& noop, Msg& m) {
+  if (w4a4_status s = kv4_attention_decode(q_f16, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, B, H,
+                                           S, D, softmax_scale, had_signs, out, noop, m))
+    return s;
+  if (noop) return W4A4_OK;
+  const int64_t need = attention_workspace_bytes(B * H, S);
+  if (workspace_bytes < need)
+    return say(m, W4A4_ERR_SHAPE, "workspace_bytes=%lld is below the %lld this shape needs (kv4_attention_workspace_bytes)",
+               (long long)workspace_bytes, (long long)need);
+  if (need > 0 && !workspace) return say(m, W4A4_ERR_NULL, "workspace must be non-NULL for this shape");
+  if (need > 0 && !aligned16(workspace)) return say(m, W4A4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return W4A4_OK;
+}
+
 inline w4a4_status rotate_quant_mxfp4(const void* x_f16, int64_t M, int64_t K, int64_t ldx, int32_t had_block,
                                       const void* had_signs, const void* codes, const void* scales_e8m0,
                                       bool& noop, Msg& m) {

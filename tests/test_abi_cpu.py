@@ -21,7 +21,8 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
               "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode",
-              "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused"):
+              "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "kv4_attention_decode_ws",
+              "kv4_attention_workspace_bytes"):
         assert n in names
 
 
@@ -29,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for n in _declared():
         assert hasattr(lib, n), n
-    assert lib.w4a4_abi_version() == 4
+    assert lib.w4a4_abi_version() == 5
     src = open(HEADER).read()
     assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
 
@@ -228,3 +229,39 @@ def test_no_device_is_a_device_error():
     st = _lib.call("rotate_quant_act", A, 4, 128, 128, 128, NUL, 0, A, A, NUL, NUL)
     assert st == _lib.W4A4_ERR_DEVICE
     assert "device" in _lib.last_error()
+
+
+@pytest.mark.parametrize("B,H,S,want", [
+    (8, 32, 4096, 0),                      # 256 heads: single pass
+    (1, 32, 4096, 32 * 8 * 528),           # ceil(256/32) = 8 ranges
+    (1, 8, 32768, 8 * 32 * 528),           # 32 ranges
+    (1, 1, 1 << 20, 64 * 528),             # capped at 64 ranges
+    (1, 2, 700, 0),                        # S / 512 = 1: single pass
+    (1, 2, 1024, 2 * 2 * 528),
+    (0, 5, 100, 0),
+])
+def test_attention_workspace_bytes(B, H, S, want):
+    assert _lib.load().kv4_attention_workspace_bytes(B, H, S) == want
+
+
+@pytest.mark.parametrize("B,H,S", [(-1, 2, 10), (1, 2, 0), (1, 2, 1 << 25), (1 << 40, 1 << 30, 10)])
+def test_attention_workspace_bytes_rejects(B, H, S):
+    assert _lib.load().kv4_attention_workspace_bytes(B, H, S) == -1
+    assert _lib.last_error()
+
+
+def _ws_args(B=1, H=8, S=32768, q=A, ws=A, nbytes=1 << 30):
+    return (q, A, A, A, A, A, A, B, H, S, 128, 0.088, NUL, A, ws, nbytes, NUL)
+
+
+@pytest.mark.parametrize("args,status", [
+    (_ws_args(nbytes=8 * 32 * 528 - 1), _lib.W4A4_ERR_SHAPE),      # workspace one byte short
+    (_ws_args(ws=NUL), _lib.W4A4_ERR_NULL),
+    (_ws_args(ws=A + 8), _lib.W4A4_ERR_ALIGN),
+    (_ws_args(q=NUL), _lib.W4A4_ERR_NULL),
+    (_ws_args(S=0), _lib.W4A4_ERR_SHAPE),
+    (_ws_args(B=0, ws=NUL, nbytes=0), _lib.W4A4_OK),                 # no heads: no-op
+    (_ws_args(B=8, H=32, S=4096, ws=NUL, nbytes=0), _lib.W4A4_ERR_DEVICE),   # single pass: no workspace needed
+])
+def test_kv4_attention_ws_validation(args, status):
+    assert _lib.call("kv4_attention_decode_ws", *args) == status

@@ -111,22 +111,86 @@ def test_attention_end_to_end_from_fp16():
 
 
 def test_attention_full_config_all_heads():
-    """The KV config (8 x 32 x 4096 x 128): GPU-quantized cache, GPU attention;
-    all 256 (batch, head) outputs checked against the oracle on the GPU's own
-    codes, one batch row at a time."""
+    """The KV config (8 x 32 x 4096 x 128) at its full launch (256 heads): the
+    oracle quantizes the cache, one batch row at a time; the GPU attends over
+    those codes; all 256 (batch, head) outputs checked against the oracle."""
     kv = WL.kv()["KV"]
     vv = np.ascontiguousarray(kv[:, ::-1])               # a second cache: heads reversed
     q = WL.small_random(123, 8 * 32, 128).reshape(8, 32, 128)
-    kc, ks, kz = R.kv_rotate_quant4(dev(kv))
-    vc, vs, vz = R.kv_rotate_quant4(dev(vv))
-    o = host(R.kv4_attention_decode(dev(q), kc, ks, kz, vc, vs, vz))
-    kc, ks, kz, vc, vs, vz = (host(t) for t in (kc, ks, kz, vc, vs, vz))
+    kqs = [_kvq(kv[b][None]) for b in range(8)]
+    vqs = [_kvq(vv[b][None]) for b in range(8)]
+    cat = lambda ds, key: np.concatenate([d[key] for d in ds], axis=0)
+    args = [dev(cat(ds, key)) for ds in (kqs, vqs) for key in ("packed", "scale", "zp")]
+    o = host(R.kv4_attention_decode(dev(q), *args))
     worst = 0.0
     for b in range(8):
-        sl = slice(b, b + 1)
-        want = O.kv4_attention_decode(q[sl], kc[sl], ks[sl], kz[sl], vc[sl], vs[sl], vz[sl],
-                                      1 / math.sqrt(128))
+        kq, vq = kqs[b], vqs[b]
+        want = O.kv4_attention_decode(q[b][None], kq["packed"], kq["scale"], kq["zp"], vq["packed"],
+                                      vq["scale"], vq["zp"], 1 / math.sqrt(128))
         for h in range(32):
             worst = max(worst, rel_fro(o[b, h], want[0, h]))
     print("all 256 heads, worst rel_fro", worst)
     assert worst <= SAME_CODES_RTOL
+
+
+# ---------------------------------------------------------------- tokens split over workgroups
+def _split_and_single(q, kq, vq, scale, d=None):
+    a = [dev(q), dev(kq["packed"]), dev(kq["scale"]), dev(kq["zp"]), dev(vq["packed"]), dev(vq["scale"]),
+         dev(vq["zp"]), scale]
+    sg = None if d is None else dev(d)
+    return host(R.kv4_attention_decode_split(*a, signs=sg)), host(R.kv4_attention_decode(*a, signs=sg))
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 2, 1024), (1, 1, 5000), (1, 8, 4097), (2, 3, 3000), (1, 4, 1000)])
+@pytest.mark.parametrize("with_signs", [False, True])
+def test_attention_split_same_codes(B, H, S, with_signs):
+    """Few heads, tokens split into ranges (ragged last range, and one case
+    below the split threshold): same-codes bound against the oracle."""
+    q, k, v = _cache(B, H, S, 7 * S + H)
+    d = WL.hadamard_signs(128, seed=H) if with_signs else None
+    kq, vq = _kvq(k, signs=d), _kvq(v, signs=d)
+    scale = 1 / math.sqrt(128)
+    o, o1 = _split_and_single(q, kq, vq, scale, d)
+    want = O.kv4_attention_decode(q, kq["packed"], kq["scale"], kq["zp"], vq["packed"], vq["scale"],
+                                  vq["zp"], scale, signs=d)
+    print(B, H, S, "ranges", R.kv4_attention_workspace_bytes(B, H, S) // (528 * B * H),
+          "split", rel_fro(o, want), "single", rel_fro(o1, want))
+    assert rel_fro(o, want) <= SAME_CODES_RTOL
+
+
+def test_attention_split_sharp_softmax():
+    """A large softmax scale: range maxima far apart, the merge rescales by 2^(m_k - M)."""
+    q, k, v = _cache(1, 2, 2600, 15)
+    kq, vq = _kvq(k), _kvq(v)
+    o, _ = _split_and_single(q, kq, vq, 2.0)
+    want = O.kv4_attention_decode(q, kq["packed"], kq["scale"], kq["zp"], vq["packed"], vq["scale"],
+                                  vq["zp"], 2.0)
+    assert rel_fro(o, want) <= SAME_CODES_RTOL
+
+
+def test_attention_split_long_context():
+    """1 x 8 heads x 32768 tokens (32 ranges per head), every head checked;
+    a caller-given workspace is used as is."""
+    q, k, v = _cache(1, 8, 32768, 21)
+    kq, vq = _kvq(k), _kvq(v)
+    need = R.kv4_attention_workspace_bytes(1, 8, 32768)
+    assert need == 8 * 32 * 528
+    ws = torch.full((need + 64,), 0x7F, dtype=torch.uint8, device="cuda")
+    a = [dev(q), dev(kq["packed"]), dev(kq["scale"]), dev(kq["zp"]), dev(vq["packed"]), dev(vq["scale"]),
+         dev(vq["zp"])]
+    o = host(R.kv4_attention_decode_split(*a, workspace=ws))
+    assert np.all(host(ws[need:]) == 0x7F), "workspace written past its size"
+    want = O.kv4_attention_decode(q, kq["packed"], kq["scale"], kq["zp"], vq["packed"], vq["scale"],
+                                  vq["zp"], 1 / math.sqrt(128))
+    worst = max(rel_fro(o[0, h], want[0, h]) for h in range(8))
+    print("long context, worst head rel_fro", worst)
+    assert worst <= SAME_CODES_RTOL
+
+
+def test_attention_split_workspace_too_small_rejected():
+    q, k, v = _cache(1, 2, 1024, 3)
+    kq, vq = _kvq(k), _kvq(v)
+    ws = torch.empty((R.kv4_attention_workspace_bytes(1, 2, 1024) - 16,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        R.kv4_attention_decode_split(dev(q), dev(kq["packed"]), dev(kq["scale"]), dev(kq["zp"]),
+                                     dev(vq["packed"]), dev(vq["scale"]), dev(vq["zp"]), workspace=ws)
