@@ -236,6 +236,66 @@ void attention_cases() {
   }
 }
 
+void split_attention_cases() {
+  // the number of token ranges: fill 256 workgroups, at least 512 tokens
+  // per range, at most 64 ranges, 1 = the single pass
+  struct N { int64_t BH, S; int32_t want; };
+  const N ns[] = {{256, 4096, 1}, {255, 1 << 20, 2}, {32, 4096, 8}, {8, 32768, 32}, {1, 1 << 20, 64},
+                  {2, 700, 1},    {2, 1024, 2},      {1, 511, 1},   {0, 10, 1},     {5, 0, 1},
+                  {int64_t(1) << 40, 10, 1}};
+  for (const N& c : ns) {
+    ++g_cases;
+    const int32_t got = w4a4v::attention_splits(c.BH, c.S);
+    if (got != c.want) {
+      ++g_fail;
+      std::printf("FAIL attention_splits(%lld, %lld) = %d, want %d\n", (long long)c.BH, (long long)c.S, got,
+                  c.want);
+    }
+    ++g_cases;
+    const int64_t bytes = w4a4v::attention_workspace_bytes(c.BH, c.S);
+    const int64_t want_bytes = c.want > 1 ? c.BH * c.want * w4a4v::kAttnPartBytes : 0;
+    if (bytes != want_bytes) {
+      ++g_fail;
+      std::printf("FAIL attention_workspace_bytes(%lld, %lld) = %lld\n", (long long)c.BH, (long long)c.S,
+                  (long long)bytes);
+    }
+  }
+  // every valid shape needs at most (BH + 255) states, BH < 256
+  int64_t most = 0;
+  for (int64_t bh = 1; bh <= 300; ++bh) {
+    const int64_t b = w4a4v::attention_workspace_bytes(bh, int64_t(1) << 24);
+    most = b > most ? b : most;
+  }
+  ++g_cases;
+  if (most != 510 * w4a4v::kAttnPartBytes) {
+    ++g_fail;
+    std::printf("FAIL largest split workspace %lld bytes\n", (long long)most);
+  }
+
+  const int64_t need = 8 * 32 * w4a4v::kAttnPartBytes;   // 1 x 8 heads x 32768 tokens
+  struct C { const char* what; int64_t B, S; const void* ws; int64_t bytes; w4a4_status want; bool noop; };
+  const C cases[] = {
+      {"ok", 1, 32768, A, need, W4A4_OK, false},
+      {"workspace one byte short", 1, 32768, A, need - 1, W4A4_ERR_SHAPE, false},
+      {"negative workspace size", 1, 32768, A, -1, W4A4_ERR_SHAPE, false},
+      {"null workspace", 1, 32768, Z, need, W4A4_ERR_NULL, false},
+      {"misaligned workspace", 1, 32768, U, need, W4A4_ERR_ALIGN, false},
+      {"single pass needs none", 32, 4096, Z, 0, W4A4_OK, false},
+      {"S == 0", 1, 0, A, need, W4A4_ERR_SHAPE, false},
+      {"B == 0", 0, 32768, Z, 0, W4A4_OK, true},
+  };
+  for (const C& c : cases) {
+    w4a4v::Msg m;
+    bool noop = true;
+    std::string what = std::string("kv4_attention_decode_ws ") + c.what;
+    expect(what.c_str(),
+           w4a4v::kv4_attention_decode_ws(A, A, A, A, A, A, A, c.B, 8, c.S, 128, 0.088f, Z, A, c.ws, c.bytes, noop,
+                                          m),
+           c.want, m);
+    expect_noop(what.c_str(), noop, c.noop);
+  }
+}
+
 void fused_cases() {
   struct C { const char* what; int64_t M, K, ldx, N, ldy; const void* x; w4a4_status want; };
   const C cases[] = {
@@ -265,6 +325,7 @@ int main() {
   gemm_cases();
   kv_cases();
   attention_cases();
+  split_attention_cases();
   fused_cases();
   if (g_fail) {
     std::printf("validate selftest: %d of %d cases failed\n", g_fail, g_cases);
