@@ -84,7 +84,7 @@ typedef enum {
 enum { W4A4_HAD_FULL = 0, W4A4_HAD_128 = 128 };              /* had_block */
 enum { W4A4_ACT_SYM_TOKEN = 0, W4A4_ACT_ASYM_G128 = 1 };     /* act_mode  */
 
-#define W4A4_ABI_VERSION 5
+#define W4A4_ABI_VERSION 6
 
 /*
  * had_signs (the rotate calls and w4a4_decode_fused): NULL, or a device array of K fp16
@@ -278,6 +278,29 @@ W4A4_API w4a4_status kv4_attention_decode_ws(const uint16_t* q_f16, const uint8_
                              int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
                              const uint16_t* had_signs, float* out, void* workspace,
                              int64_t workspace_bytes, void* stream);
+
+/*
+ * kv4_attention_decode_noalloc - kv4_attention_decode_ws for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels, the same result,
+ * with the partial states kept in a static device array of the library
+ * instead of a caller's workspace.  The call itself allocates nothing.
+ *
+ *   Limit: that array holds 524,288 bytes (512 KiB) on each GPU the library
+ *   runs on, kept until the process ends; a shape whose
+ *   kv4_attention_workspace_bytes(B, H, S) exceeds it is refused with
+ *   W4A4_ERR_SHAPE (no valid shape needs more than 269,280 bytes).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in
+ *   time on one GPU (two streams, two threads) race and give wrong output;
+ *   order them on one stream.  Nothing in the array needs to start at zero:
+ *   each call writes every state it later reads.
+ * Arguments, rules and output as kv4_attention_decode.
+ */
+W4A4_API w4a4_status kv4_attention_decode_noalloc(const uint16_t* q_f16, const uint8_t* k_codes,
+                             const float* k_scales, const uint8_t* k_zeros,
+                             const uint8_t* v_codes, const float* v_scales, const uint8_t* v_zeros,
+                             int64_t B, int64_t H, int64_t S, int64_t D, float softmax_scale,
+                             const uint16_t* had_signs, float* out, void* stream);
 
 /*
  * rotate_quant_mxfp4 - the rotate step with MXFP4 output: per row, the same

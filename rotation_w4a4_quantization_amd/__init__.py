@@ -15,6 +15,7 @@ exception.  Every step of the computation runs in the library's kernels.
     kc, ks, kz = kv_rotate_quant4(kv)
     o = kv4_attention_decode(q, kc, ks, kz, vc, vs, vz)   # decode attention on the INT4 cache
     o = kv4_attention_decode_split(q, kc, ks, kz, vc, vs, vz)   # the same, tokens split (few heads)
+    o = kv4_attention_decode_noalloc(q, kc, ks, kz, vc, vs, vz, out=o)  # split, library's static scratch
     # MXFP4 (E2M1 codes, a power-of-two scale per 32) on the scaled FP4 MFMA
     xc, xe = rotate_quant_mxfp4(x, had_block=128)
     wc, we = rotate_quant_mxfp4(w, had_block=128)
@@ -30,6 +31,7 @@ from ._lib import (W4A4_ACT_ASYM_G128, W4A4_ACT_SYM_TOKEN, W4A4_HAD_128, W4A4_HA
 
 __all__ = ["rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
            "kv4_attention_decode", "kv4_attention_decode_split", "kv4_attention_workspace_bytes",
+           "kv4_attention_decode_noalloc",
            "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "abi_version", "W4A4Error"]
 
 _MODES = {"sym": W4A4_ACT_SYM_TOKEN, "asym": W4A4_ACT_ASYM_G128}
@@ -248,9 +250,19 @@ def kv4_attention_decode_split(q: torch.Tensor, k_codes, k_scales, k_zeros, v_co
                                 out, _split=True, _workspace=workspace)
 
 
+def kv4_attention_decode_noalloc(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
+                                 softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None):
+    """kv4_attention_decode_split with the partial states in the library's
+    static device scratch (kv4_attention_decode_noalloc): the library
+    allocates nothing.  Pass `out` (fp32 [B, H, 128]) to allocate nothing
+    here either.  Calls that overlap in time on one GPU race."""
+    return kv4_attention_decode(q, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, softmax_scale, signs,
+                                out, _split="static")
+
+
 def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros,
                          softmax_scale: float | None = None, signs=None, out: torch.Tensor | None = None,
-                         _split: bool = False, _workspace: torch.Tensor | None = None):
+                         _split: bool | str = False, _workspace: torch.Tensor | None = None):
     """Single-query attention per (batch, head) over a KV cache written by
     kv_rotate_quant4 (rotated asymmetric INT4); q fp16 [B, H, 128].
 
@@ -280,6 +292,12 @@ def kv4_attention_decode(q: torch.Tensor, k_codes, k_scales, k_zeros, v_codes, v
     if tuple(y.shape) != (B, H, D) or not y.is_contiguous():
         raise ValueError("out must be a contiguous [B, H, D] fp32 tensor")
     sg = _signs(signs, D, dev)
+    if _split == "static":
+        st = _lib.call("kv4_attention_decode_noalloc", _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(k_zeros),
+                       _ptr(v_codes), _ptr(v_scales), _ptr(v_zeros), B, H, S, D, scale, _ptr(sg), _ptr(y),
+                       _stream(dev))
+        _check(st, "kv4_attention_decode_noalloc")
+        return y
     if _split:
         need = kv4_attention_workspace_bytes(B, H, S) if B * H > 0 else 0
         ws = _workspace

@@ -33,6 +33,8 @@ SIGNATURES = {
     "mxfp4_gemm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "kv4_attention_decode_ws": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
                                 _vp, _vp, _vp, _i64, _vp],
+    "kv4_attention_decode_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                     _vp, _vp, _vp],
 }
 # entry points that return a value other than a status
 SIZE_FUNCS = {"kv4_attention_workspace_bytes": [_i64, _i64, _i64]}

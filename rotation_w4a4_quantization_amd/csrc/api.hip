@@ -49,6 +49,15 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
 
+// Partial states of kv4_attention_decode_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address); it uses the address hipGetSymbolAddress gives for each device.
+// The split path needs at most 510 states of 528 bytes (269,280 bytes).
+constexpr int64_t kScratchBytes = int64_t(512) << 10;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+void* g_scratch[kMaxDevices];   // device address of `scratch` on each device (under g_dev_mu)
+
 // The code objects are built for gfx950 only: refuse any other device up
 // front instead of failing inside a launch.
 w4a4_status check_device() {
@@ -66,15 +75,27 @@ w4a4_status check_device() {
       g_dev_state[dev] = -1;
       return verdict(W4A4_ERR_DEVICE, m);
     }
-    g_dev_state[dev] = 1;
-    if (w4a4::gemm_prepare_device() != hipSuccess) {
-      g_dev_state[dev] = 0;
+    if (w4a4::gemm_prepare_device() != hipSuccess)
       return fail(W4A4_ERR_DEVICE, "could not raise the LDS limit of the GEMM kernels");
-    }
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(W4A4_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+    g_dev_state[dev] = 1;
   }
   if (g_dev_state[dev] != 1)
     return fail(W4A4_ERR_DEVICE, "device %d is not gfx950; this library is built for gfx950 only", dev);
   return W4A4_OK;
+}
+
+// The current device's address of `scratch` (check_device() has set it).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  return g_scratch[dev];
 }
 
 w4a4_status launched(hipError_t e, const char* what) {
@@ -380,6 +401,40 @@ w4a4_status kv4_attention_decode_ws(const uint16_t* q_f16, const uint8_t* k_code
   p.nsplit = w4a4v::attention_splits(p.BH, S);
   p.part = static_cast<float*>(workspace);
   return launched(w4a4::launch_kv4_attention_split(p, (hipStream_t)stream), "kv4_attention_decode_ws");
+}
+
+w4a4_status kv4_attention_decode_noalloc(const uint16_t* q_f16, const uint8_t* k_codes, const float* k_scales,
+                                         const uint8_t* k_zeros, const uint8_t* v_codes, const float* v_scales,
+                                         const uint8_t* v_zeros, int64_t B, int64_t H, int64_t S, int64_t D,
+                                         float softmax_scale, const uint16_t* had_signs, float* out, void* stream) {
+  TimingScope timing_scope;
+  w4a4v::Msg m;
+  bool noop = false;
+  if (w4a4_status s = w4a4v::kv4_attention_decode_noalloc(q_f16, k_codes, k_scales, k_zeros, v_codes, v_scales,
+                                                          v_zeros, B, H, S, D, softmax_scale, had_signs, out,
+                                                          kScratchBytes, noop, m))
+    return verdict(s, m);
+  if (noop) return ok();
+  if (w4a4_status s = check_device()) return s;
+  void* part = device_scratch();
+  if (!part) return fail(W4A4_ERR_DEVICE, "no scratch address for the current device");
+
+  w4a4::AttnParams p{};
+  p.q = q_f16;
+  p.k_codes = k_codes;
+  p.k_scales = k_scales;
+  p.k_zeros = k_zeros;
+  p.v_codes = v_codes;
+  p.v_scales = v_scales;
+  p.v_zeros = v_zeros;
+  p.signs = had_signs;
+  p.out = out;
+  p.BH = B * H;
+  p.S = S;
+  p.scale2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.nsplit = w4a4v::attention_splits(p.BH, S);
+  p.part = static_cast<float*>(part);
+  return launched(w4a4::launch_kv4_attention_split(p, (hipStream_t)stream), "kv4_attention_decode_noalloc");
 }
 
 }  // extern "C"

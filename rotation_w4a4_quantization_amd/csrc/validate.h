@@ -249,6 +249,26 @@ inline w4a4_status kv4_attention_decode_ws(const void* q_f16, const void* k_code
   return W4A4_OK;
 }
 
+// The allocation-free variant keeps the partial states in a static device
+// array of scratch_bytes; a shape that needs more is refused.
+inline w4a4_status kv4_attention_decode_noalloc(const void* q_f16, const void* k_codes, const void* k_scales,
+                                                const void* k_zeros, const void* v_codes, const void* v_scales,
+                                                const void* v_zeros, int64_t B, int64_t H, int64_t S, int64_t D,
+                                                float softmax_scale, const void* had_signs, const void* out,
+                                                int64_t scratch_bytes, bool& noop, Msg& m) {
+  if (w4a4_status s = kv4_attention_decode(q_f16, k_codes, k_scales, k_zeros, v_codes, v_scales, v_zeros, B, H,
+                                           S, D, softmax_scale, had_signs, out, noop, m))
+    return s;
+  if (noop) return W4A4_OK;
+  const int64_t need = attention_workspace_bytes(B * H, S);
+  if (need > scratch_bytes)
+    return say(m, W4A4_ERR_SHAPE,
+               "this shape needs %lld bytes of partial states, more than the %lld-byte static scratch of "
+               "kv4_attention_decode_noalloc (use kv4_attention_decode_ws)",
+               (long long)need, (long long)scratch_bytes);
+  return W4A4_OK;
+}
+
 inline w4a4_status rotate_quant_mxfp4(const void* x_f16, int64_t M, int64_t K, int64_t ldx, int32_t had_block,
                                       const void* had_signs, const void* codes, const void* scales_e8m0,
                                       bool& noop, Msg& m) {

@@ -22,7 +22,7 @@ def test_header_declares_the_four_calls():
     for n in ("rotate_quant_act", "quant_weight_offline", "w4a4_gemm", "kv_rotate_quant4",
               "w4a4_last_error", "w4a4_abi_version", "w4a4_time_next_launch", "kv4_attention_decode",
               "rotate_quant_mxfp4", "mxfp4_gemm", "w4a4_decode_fused", "kv4_attention_decode_ws",
-              "kv4_attention_workspace_bytes"):
+              "kv4_attention_workspace_bytes", "kv4_attention_decode_noalloc"):
         assert n in names
 
 
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for n in _declared():
         assert hasattr(lib, n), n
-    assert lib.w4a4_abi_version() == 5
+    assert lib.w4a4_abi_version() == 6
     src = open(HEADER).read()
     assert int(re.search(r"#define W4A4_ABI_VERSION (\d+)", src).group(1)) == lib.w4a4_abi_version()
 
@@ -265,3 +265,13 @@ def _ws_args(B=1, H=8, S=32768, q=A, ws=A, nbytes=1 << 30):
 ])
 def test_kv4_attention_ws_validation(args, status):
     assert _lib.call("kv4_attention_decode_ws", *args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, A, A, A, 1, 8, 32768, 128, 0.088, NUL, A, NUL), _lib.W4A4_ERR_DEVICE),   # valid: reaches the device check
+    ((NUL, A, A, A, A, A, A, 1, 8, 32768, 128, 0.088, NUL, A, NUL), _lib.W4A4_ERR_NULL),
+    ((A, A, A, A, A, A, A, 1, 8, 0, 128, 0.088, NUL, A, NUL), _lib.W4A4_ERR_SHAPE),
+    ((A, A, A, A, A, A, A, 0, 8, 100, 128, 0.088, NUL, A, NUL), _lib.W4A4_OK),             # no heads: no-op
+])
+def test_kv4_attention_noalloc_validation(args, status):
+    assert _lib.call("kv4_attention_decode_noalloc", *args) == status
