@@ -260,8 +260,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 #pragma unroll
   for (int i = 0; i < TM; ++i) arow[i] = (wave * 16 * TM + 16 * i + fr) * G;
 
-  // A codes, zero-points and scales of a group travel together, loaded one
-  // group ahead of their use (right after the step before it); all are
+  // A codes, zero-points and scales of a group travel together in one of
+  // two register sets, loaded two groups ahead of their use (right after the
+  // step that emptied the set, so a whole step hides the load); all are
   // buffer loads (no branches, so no wait is forced until the step that
   // consumes them)
   uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
@@ -375,34 +376,40 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
       for (int j = 0; j < 8; ++j) fold(i, j, sf[i]);
   };
 
-  // Group g's codes, zero-points and scales sit in register set g & 1; group
-  // g's step folds group g-1 with the scales of set (g-1) & 1, which is
-  // refilled right afterwards with group g+1's data (one group ahead).  Set
-  // 1 starts with zero scales.
+  // Group g's codes, zero-points and scales sit in register set g & 1.
+  // Group g's step folds group g-1 with the scales held in sp; after the
+  // step, sp takes group g's scales and set g & 1 is refilled with group
+  // g+2.  sp starts at zero.
+  float sp[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) s1[i] = 0.0f;
+  for (int i = 0; i < TM; ++i) sp[i] = 0.0f;
   load_a(pa0, z0, s0, 0);
+  load_a(pa1, z1, s1, 1);
   load_b(pb0, 0);
   load_b(pb1, 1);
   store_b(pb0, 0);
   __syncthreads();
   for (int kt = 0; kt + 1 < nkt; kt += 2) {
     load_b(pb0, kt + 2);
-    step(pa0, z0, s1, 0);             // group kt; fold of group kt - 1
-    load_a(pa1, z1, s1, kt + 1);
+    step(pa0, z0, sp, 0);             // group kt; fold of group kt - 1
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sp[i] = s0[i];
+    load_a(pa0, z0, s0, kt + 2);
     store_b(pb1, 1);
     __syncthreads();
     load_b(pb1, kt + 3);
-    step(pa1, z1, s0, 1);             // group kt + 1; fold of group kt
-    load_a(pa0, z0, s0, kt + 2);
+    step(pa1, z1, sp, 1);             // group kt + 1; fold of group kt
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sp[i] = s1[i];
+    load_a(pa1, z1, s1, kt + 3);
     store_b(pb0, 0);
     __syncthreads();
   }
   if (nkt & 1) {
-    step(pa0, z0, s1, 0);             // group nkt - 1; fold of group nkt - 2
+    step(pa0, z0, sp, 0);             // group nkt - 1; fold of group nkt - 2
     fold_all(s0);
   } else {
-    fold_all(s1);                     // group nkt - 1
+    fold_all(sp);                     // group nkt - 1
   }
 
   // the accumulators hold 16 x the levels' products: the exact power-of-two
