@@ -294,6 +294,27 @@ void split_attention_cases() {
            c.want, m);
     expect_noop(what.c_str(), noop, c.noop);
   }
+
+  // the allocation-free variant: the same rules, and the partial states must
+  // fit its static scratch (a small limit here forces the refusal)
+  struct N2 { const char* what; int64_t B, S, limit; w4a4_status want; bool noop; };
+  const N2 na[] = {
+      {"fits", 1, 32768, need, W4A4_OK, false},
+      {"one byte over the scratch", 1, 32768, need - 1, W4A4_ERR_SHAPE, false},
+      {"single pass needs no scratch", 32, 4096, 0, W4A4_OK, false},
+      {"S == 0", 1, 0, need, W4A4_ERR_SHAPE, false},
+      {"B == 0", 0, 32768, 0, W4A4_OK, true},
+      {"largest need fits 512 KiB", 1, int64_t(1) << 24, 512 * 1024, W4A4_OK, false},
+  };
+  for (const N2& c : na) {
+    w4a4v::Msg m;
+    bool noop = true;
+    std::string what = std::string("kv4_attention_decode_noalloc ") + c.what;
+    expect(what.c_str(),
+           w4a4v::kv4_attention_decode_noalloc(A, A, A, A, A, A, A, c.B, 8, c.S, 128, 0.088f, Z, A, c.limit, noop, m),
+           c.want, m);
+    expect_noop(what.c_str(), noop, c.noop);
+  }
 }
 
 void fused_cases() {
