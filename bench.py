@@ -58,7 +58,7 @@ def profile_traffic(kernel_key: str, src: str):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_src = re.search(r"source_hash:\s*(\w+)", txt)
+    m_src = re.search(r"source_hash(?:\s*\([^)]*\))?:\s*(\w+)", txt)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     if not m_src or not m_b or m_src.group(1) != src:
         return None

@@ -57,3 +57,13 @@ def test_bench_line_fields():
     M, N, K = d["config"]["M"], d["config"]["N"], d["config"]["K"]
     assert abs(d["value"] - 2 * M * N * K / (d["ms_per_step"] * 1e-3) / 1e12) / d["value"] < 0.01
     assert d["value"] < rf["achieved"]
+
+
+def test_committed_gemm_profile_gives_the_traffic_figure():
+    """The bench line's roofline.traffic comes from the committed q_proj GEMM
+    profile while its source hash matches the current GEMM sources."""
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.profile_traffic("w4a4_gemm_qproj_had128", bench.src_hash("gemm.hip", "common.h", "tile.h"))
+    assert t is not None and t > 0
+    assert bench.profile_traffic("w4a4_gemm_qproj_had128", "0" * 16) is None
