@@ -250,7 +250,7 @@ def test_mxfp4_gemm_empty():
 
 
 # ---------------------------------------------------------------- end to end
-@pytest.mark.parametrize("cfg", ["tiny", "qproj"])
+@pytest.mark.parametrize("cfg", ["tiny", "qproj", "downproj", "gateup"])
 def test_mxfp4_linear_end_to_end(cfg):
     """X and W rotated and quantized to MXFP4 on the GPU, then multiplied:
     the product agrees with the oracle's whole pipeline to 1e-3 relative
@@ -261,7 +261,14 @@ def test_mxfp4_linear_end_to_end(cfg):
         X, W = d["X"], d["W"]
         rows, cols = np.arange(X.shape[0]), np.arange(W.shape[0])
     else:
-        X, W = WL.qproj(with_w=False)["X"], WL.qproj_weight()
+        # full-size GEMM (the 8-wave 256-row instance from 512 tiles up, the
+        # 16-wave one below), checked on sampled rows and columns
+        if cfg == "qproj":
+            X, W = WL.qproj(with_w=False)["X"], WL.qproj_weight()
+        else:
+            d = WL.downproj() if cfg == "downproj" else WL.gateup()
+            X, W = d["X"], d["W"]
+            del d
         rng = np.random.default_rng(6)
         rows = np.sort(rng.choice(X.shape[0], 64, replace=False))
         cols = np.sort(rng.choice(W.shape[0], 256, replace=False))
