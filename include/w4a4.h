@@ -231,6 +231,10 @@ W4A4_API w4a4_status kv_rotate_quant4(const uint16_t* kv_f16, int64_t B, int64_t
  *   softmax_scale  finite, > 0 (typically 1/sqrt(128)).
  *   had_signs NULL, or the fp16 +-1 vector [128] the cache was rotated with.
  *   out       [B][H][128] fp32 (written).
+ * Arithmetic: the scores take the rotated query in 20-bit fixed point
+ * (q ~ sq * qi, |qi| <= 2^19 - 1, sq = max|q| / (2^19 - 1): at most 2^-20 of
+ * max|q| per element) on exact integer dot products with the codes; the
+ * softmax and the weighted value sum are fp32.
  * One workgroup per (b, h); every token's codes are read once.
  */
 W4A4_API w4a4_status kv4_attention_decode(const uint16_t* q_f16, const uint8_t* k_codes,

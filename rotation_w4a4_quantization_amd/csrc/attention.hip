@@ -16,7 +16,8 @@
 // token per step and lane j = lane % 4 of the group holds dimensions
 // 32 j .. 32 j + 31 (16 bytes of codes).  The kernel is VALU-bound, so the
 // per-token bookkeeping is shared by as few lanes as registers allow (4),
-// and the running output is rescaled only when a running maximum grows.
+// and a lane group's running output is rescaled only when a score exceeds
+// its reference maximum by more than 2^8.
 // Dequantized values are s (u - z); the zero-point parts are factored out:
 //   score  = scale * s_k * (sum_d q_d u_d - z_k * sum_d q_d)
 //   o_rot  = sum_t p_t s_v,t u_t  -  (sum_t p_t s_v,t z_v,t) * 1
