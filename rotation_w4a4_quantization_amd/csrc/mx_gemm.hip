@@ -18,8 +18,8 @@
 // column r.  The prefill kernel passes the weight fragment first and the
 // activation fragment second, so C's rows are output columns: lane (r, g)
 // holds output row r, columns 4 g .. 4 g + 3 (16 contiguous bytes).  The
-// packed operands keep the INT4 kernels' tiling: A rows straight from
-// global memory into registers, B rows staged through LDS.
+// packed operands need no widening, so both go from global memory straight
+// into LDS (see the prefill kernel) and are read back in this lane layout.
 //
 // Exponent bytes: a row holds 4 per 128-wide K step, [4 kt + g].  A lane
 // loads the 16 bytes of four steps of its row at once and gathers the 4
@@ -36,6 +36,7 @@ namespace w4a4 {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBN = 128;       // output columns per workgroup
 constexpr int kKS = 128;       // K elements per step (64 packed bytes of a row)
@@ -48,6 +49,15 @@ constexpr int kRow = 64;       // LDS bytes of one B row per step
 // with row & 3, (row >> 2) & 3 or ((row >> 1) ^ (row >> 3)) & 3, and 80-byte
 // padding all read at 108-116 B/clk/CU.
 __device__ __forceinline__ int mx_chunk(int row, int c) { return row * kRow + ((c ^ ((row >> 1) & 3)) << 4); }
+
+// Workgroup barrier for the prefill kernel's LDS stages: this wave's LDS
+// operations complete and at most N of its vector-memory operations remain in
+// flight, then s_barrier.  No memory fence: a __syncthreads would also wait
+// for the loads of later steps that are still on their way.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // One 16x16x128 FP4 x FP4 product with per-lane E8M0 scales; SEL picks the
 // scale byte inside the scale dwords.
@@ -85,23 +95,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 
 // ---------------------------------------------------------------- prefill kernel
 // BM x 128 output tile per workgroup, NW waves stacked along M, each wave
-// 16*TM rows x 128 columns (TM x 8 products of 16x16 per step).  Steps are
-// walked in groups of four (the four bytes of an exponent dword); A is
-// loaded two steps ahead into registers, B two steps ahead into registers
-// and one step ahead into a double-buffered LDS stage, and the exponents of
-// B (shared by every wave) one group ahead into a double-buffered LDS table.
-// A step past the end of K is loaded (harmlessly, inside or past the
-// operand's range) but not multiplied.
+// 16*TM rows x 128 columns (TM x 8 products of 16x16 per step).
+//
+// Both operands go from global memory straight into LDS with gfx950's
+// buffer_load_dwordx4 ... lds: one such load writes the 16 bytes of lane l at
+// LDS offset 16 l of its destination, so no register staging and no LDS
+// store instruction are needed.  Each lane is given the global address whose
+// bytes belong at its LDS position:
+//   - A (private to each wave, 16 rows per load): lane 4 r + c' reads chunk
+//     c' ^ ((r >> 2) & 3) of row r, so that the fragment reads below (lane
+//     16 g + r reads chunk g of row r) hit 16 distinct bank groups;
+//   - B (shared, each wave moves 128 / NW rows, 16 per load): lane 4 r + c'
+//     reads chunk c' ^ ((row >> 1) & 3), the layout of mx_chunk.
+// Four adjacent lanes thus read one 64-byte row segment.  Registers loaded
+// straight in the MFMA layout (lane 16 g + r reading row r, adjacent lanes in
+// 16 different rows) cost the load path about 2.7 times this order's time.
+//
+// Steps are walked in groups of four (the four bytes of an exponent dword).
+// Each operand has four LDS stages, step t in stage t & 3, each its own array
+// so that the compiler's waits for a stage's loads are exact; the loads of
+// step t + 2 are issued at the start of step t, into the stage step t - 2
+// used.  At the end of step t the wave waits for its own share of B step t + 1
+// (every vector-memory operation it issued after that share belongs to step t:
+// KS loads, KG at a group start, where the next group's exponents are loaded
+// too), then the workgroup barrier makes the whole stage visible.  The
+// exponents of B (shared by every wave) go through a double-buffered LDS
+// table once per group.  A step past the end of K is loaded (harmlessly,
+// inside or past the operand's range) but not multiplied.
 template <int NW, int TM, int WPE>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   constexpr int BMD = NW * 16 * TM;
   constexpr int NT = NW * 64;
-  static_assert(NT == 1024 || (NT <= 512 && 512 % NT == 0), "B staging: 512 chunks per step");
-  constexpr int NCB = NT >= 512 ? 1 : 512 / NT;   // 16-byte B chunks per thread and step (128 rows x 4)
-  const bool b_stager = NT <= 512 || threadIdx.x < 512;   // with 1024 threads, half of them stage B
+  static_assert(NW == 4 || NW == 8, "B: 16 or 32 rows per wave and step");
+  constexpr int BPW = 128 / (16 * NW);      // B loads per wave and step
+  constexpr int KS = TM + BPW;              // vector-memory operations per step
+  constexpr int KG = KS + TM;               // ... at a group start (plus the A exponents)
   constexpr int BSTAGE = 128 * kRow;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
+  constexpr int ASTAGE = NW * TM * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[ASTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[ASTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[ASTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa3[ASTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[BSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[BSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sb2[BSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sb3[BSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t bexp[2][128 * 4];   // [group parity][B row][block g]
 
   const int tid = threadIdx.x;
@@ -110,7 +149,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   const int64_t tiles_n = (p.N + kBN - 1) / kBN;
   const int64_t tiles_m = (p.M + BMD - 1) / BMD;
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * BMD, n0 = tn * kBN;
   const int nkt = p.K / kKS;
   const int ngr = (nkt + 3) / 4;
@@ -122,37 +161,28 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   const __amdgpu_buffer_rsrc_t rbe = rsrc(p.we + n0 * lde, (p.N - n0) * lde);
 
   const int fr = lane & 15, g = lane >> 4;
-  const int a_off = (wave * 16 * TM + fr) * (int)ldc + 16 * g;   // + 16 i ldc + 64 kt
+  const int lr = lane >> 2;                                      // row of this lane's loads
+  const int a_goff = (wave * 16 * TM + lr) * (int)ldc + 16 * ((lane & 3) ^ ((lr >> 2) & 3));
+  const int a_roff = wave * TM * 1024 + 64 * fr + 16 * (g ^ ((fr >> 2) & 3));
+  const int b_row = wave * 16 * BPW + lr;
+  const int b_goff = b_row * (int)ldc + 16 * ((lane & 3) ^ ((b_row >> 1) & 3));
   const int ae_off = (wave * 16 * TM + fr) * (int)lde;           // + 16 i lde + 16 u
   const uint32_t gsel = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0C0C0000u;
-  int b_off[NCB], b_lds[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    const int cb = tid + NT * j;
-    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
-    b_lds[j] = mx_chunk(cb >> 2, cb & 3);
-  }
   const int bf = mx_chunk(fr, g);        // fragment of column block j at bf + j * 16 * kRow
   const bool be_stager = tid < 128;      // thread t stages the exponents of B row t
 
-  uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB], ae_raw[TM], be_raw;
+  uint4 ae_raw[TM], be_raw;
   uint32_t ae[TM], be[8];
 
-  auto load_a = [&](uint4* pa, int kt) {
+  auto issue = [&](uint8_t* sa, uint8_t* sb, int kt) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
-  };
-  auto load_b = [&](uint4* pb, int kt) {
-    if (!b_stager) return;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + wave * TM * 1024 + i * 1024), 16,
+                                               a_goff + i * 16 * (int)ldc + kt * 64, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < NCB; ++j)
-      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
-  };
-  auto store_b = [&](const uint4* pb, int stage) {
-    if (!b_stager) return;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) *reinterpret_cast<uint4*>(smem + stage * BSTAGE + b_lds[j]) = pb[j];
+    for (int q = 0; q < BPW; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + (wave * BPW + q) * 1024), 16,
+                                               b_goff + q * 16 * (int)ldc + kt * 64, 0, 0, 0);
   };
   auto load_exps = [&](int u) {
 #pragma unroll
@@ -177,14 +207,16 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](auto sel, const uint4* pa, int stage) {
+  auto compute = [&](auto sel, const uint8_t* sa, const uint8_t* sb) {
     constexpr int S = decltype(sel)::value;
-    const uint8_t* Bs = smem + stage * BSTAGE;
+    uint4 a[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const uint4*>(sa + a_roff + i * 1024);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint4 b = *reinterpret_cast<const uint4*>(Bs + j * 16 * kRow + bf);
+      const uint4 b = *reinterpret_cast<const uint4*>(sb + j * 16 * kRow + bf);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][j] = mfma_mx<S>(b, be[j], pa[i], ae[i], acc[i][j]);
+      for (int i = 0; i < TM; ++i) acc[i][j] = mfma_mx<S>(b, be[j], a[i], ae[i], acc[i][j]);
     }
   };
   using S0 = std::integral_constant<int, 0>;
@@ -192,43 +224,47 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
 
-  // prologue: exponents of group 0, A and B steps 0 and 1 in flight, B step 0
-  // and the B exponents of group 0 in LDS
+  // prologue: exponents of group 0, steps 0 and 1 on their way, B exponents
+  // of group 0 in LDS, this wave's share of B step 0 landed
   load_exps(0);
-  load_a(pa0, 0);
-  load_b(pb0, 0);
-  load_a(pa1, 1);
-  load_b(pb1, 1);
+  issue(sa0, sb0, 0);
+  issue(sa1, sb1, 1);
   store_bexp(0);
-  store_b(pb0, 0);
-  __syncthreads();
-  for (int u = 0; u < ngr; ++u) {
+  stage_barrier<KS>();
+  // one group of four steps; FULL: all four lie inside K.  The scheduling
+  // fences keep each step's loads ahead of its multiplications, where the
+  // barrier counts expect them.
+  auto group = [&](int u, auto FULL) {
+    constexpr bool full = decltype(FULL)::value;
     const int kt = 4 * u;
     const int par = u & 1;
     take_exps(par);                   // this group's exponents into registers ...
     load_exps(u + 1);                 // ... and the next group's on their way
-    load_b(pb0, kt + 2);
-    compute(S0{}, pa0, 0);            // step kt (always < nkt)
-    load_a(pa0, kt + 2);
-    store_b(pb1, 1);                  // B step kt+1
-    __syncthreads();
-    load_b(pb1, kt + 3);
-    if (kt + 1 < nkt) compute(S1{}, pa1, 1);
-    load_a(pa1, kt + 3);
-    store_b(pb0, 0);                  // B step kt+2
+    issue(sa2, sb2, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(S0{}, sa0, sb0);          // step kt (always < nkt)
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier<KG>();
+    issue(sa3, sb3, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (full || kt + 1 < nkt) compute(S1{}, sa1, sb1);
+    __builtin_amdgcn_sched_barrier(0);
     store_bexp(par ^ 1);              // B exponents of group u+1 (the other table was last read in group u-1)
-    __syncthreads();
-    load_b(pb0, kt + 4);
-    if (kt + 2 < nkt) compute(S2{}, pa0, 0);
-    load_a(pa0, kt + 4);
-    store_b(pb1, 1);                  // B step kt+3
-    __syncthreads();
-    load_b(pb1, kt + 5);
-    if (kt + 3 < nkt) compute(S3{}, pa1, 1);
-    load_a(pa1, kt + 5);
-    store_b(pb0, 0);                  // B step kt+4
-    __syncthreads();
-  }
+    stage_barrier<KS>();
+    issue(sa0, sb0, kt + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    if (full || kt + 2 < nkt) compute(S2{}, sa2, sb2);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier<KS>();
+    issue(sa1, sb1, kt + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    if (full || kt + 3 < nkt) compute(S3{}, sa3, sb3);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier<KS>();
+  };
+  const int nfull = nkt / 4;
+  for (int u = 0; u < nfull; ++u) group(u, std::true_type{});
+  if (nfull < ngr) group(nfull, std::false_type{});
 
   // epilogue: lane (fr, g) holds Y[m0 + wave*16*TM + 16 i + fr][n0 + 16 j +
   // 4 g + v] of block (i, j); pairs of blocks go out as full 128-byte rows
@@ -322,14 +358,10 @@ hipError_t launch_mx_gemm(const MxGemmParams& p, hipStream_t st) {
     const int64_t grid = (p.N + 15) / 16;
     W4A4_LAUNCH(mx_gemm_decode_kernel, dim3((uint32_t)grid), dim3(256), 0, st, p);
   } else if (((p.M + 255) / 256) * ((p.N + kBN - 1) / kBN) >= 256) {
-    // 256-row tiles: 8 waves of 32 rows when there are at least two tiles per
-    // CU, else 16 waves of 16 rows so that one workgroup per CU still has
-    // four waves per SIMD; fewer than one such tile per CU: 64-row tiles
+    // 256-row tiles of 8 waves (32 rows each) from one tile per CU up; fewer:
+    // 64-row tiles of 4 waves, so that small shapes still spread over the CUs
     const int64_t grid = ((p.M + 255) / 256) * ((p.N + kBN - 1) / kBN);
-    if (grid >= 512)
-      W4A4_LAUNCH((mx_gemm_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
-    else
-      W4A4_LAUNCH((mx_gemm_kernel<16, 1, 4>), dim3((uint32_t)grid), dim3(1024), 0, st, p);
+    W4A4_LAUNCH((mx_gemm_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
   } else {
     const int64_t grid = ((p.M + 63) / 64) * ((p.N + kBN - 1) / kBN);
     W4A4_LAUNCH((mx_gemm_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);

@@ -20,31 +20,13 @@ __device__ __forceinline__ v4i mfma16(const v4i& a, const v4i& b, const v4i& c) 
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Tile coordinates of this workgroup.  Tiles are walked in groups of 16 tile
-// rows, column by column inside a group, so the workgroups resident at one
-// time cover a 16-row block of tiles and share both its A rows and its B
-// rows in L2 (row-major order would stream every B tile once per pair of
-// tile rows); measured 2-5% faster on the q_proj, down_proj and gate/up
-// shapes.  The mapping is a bijection of [0, tiles_m * tiles_n).
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  constexpr int64_t GM = 16;
-  const int64_t pid = blockIdx.x;
-  const int64_t in_group = GM * tiles_n;
-  const int64_t gid = pid / in_group;
-  const int64_t first_m = gid * GM;
-  const int64_t gsz = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-  const int64_t r = pid - gid * in_group;
-  tm = first_m + r % gsz;
-  tn = r / gsz;
-}
-
 // XCD-aware tile coordinates.  Workgroup i of a launch runs on XCD i % 8 of
 // the 8 that share the chip, and each XCD has its own L2.  The first
 // 8 * floor(T / 8) workgroups are renumbered so that XCD x receives the
 // contiguous range [x T8/8, (x + 1) T8/8) of a grouped order with groups of
 // 4 tile rows, i.e. compact blocks of tiles whose A and B rows its L2 shares
 // (measured on the q_proj and 8192 x 4096 x 4096 shapes: 2-4% faster than
-// the 16-row grouped order with no renumbering).  The remaining T % 8
+// a grouped order of 16 tile rows with no renumbering).  The remaining T % 8
 // workgroups keep their own index.  The mapping is a bijection of [0, T).
 __device__ __forceinline__ void tile_coords_xcd(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
   constexpr int64_t GM = 4;
