@@ -212,6 +212,26 @@ def test_mxfp4_gemm_rounding_bound(M, N, K):
     print(M, N, K, "rel_fro", r)
 
 
+@pytest.mark.parametrize("M,N,K,exact", [(2048, 4096, 384, True), (2048, 4096, 1152, False),
+                                         (2304, 4096, 640, False)])
+def test_mxfp4_gemm_one_tile_per_cu(M, N, K, exact):
+    """The 256-row instance (one or more tiles per CU) over full groups of four
+    K-steps and a partial last group (K/128 = 3, 9, 5), checked on sampled rows
+    that include the first and last row of every 256-row tile: exactly for
+    K <= 384 with exponents in [-2, 2], else to the fp32 accumulation bound."""
+    s = M + 3 * N + K
+    px, pw = WL.random_bytes(s, M, K // 2), WL.random_bytes(s + 1, N, K // 2)
+    lo, hi = (125, 129) if exact else (117, 137)
+    bx, bw = WL.random_bytes(s + 2, M, K // 32, lo, hi), WL.random_bytes(s + 3, N, K // 32, lo, hi)
+    y = host(R.mxfp4_gemm(dev(px), dev(bx), dev(pw), dev(bw)))
+    edges = np.concatenate([np.arange(0, M, 256), np.minimum(np.arange(255, M + 255, 256), M - 1)])
+    rest = np.random.default_rng(s).choice(M, 256 - len(np.unique(edges)), replace=False)
+    rows = np.unique(np.concatenate([edges, rest]))
+    r = check_product(y[rows], mx_codes(px[rows]), bx[rows].astype(np.int64) - 127, mx_codes(pw),
+                      bw.astype(np.int64) - 127, exact=exact)
+    print(M, N, K, "rows", len(rows), "rel_fro", r)
+
+
 def test_mxfp4_gemm_output_stride():
     M, N, K = 40, 96, 256
     px, pw = WL.random_bytes(1, M, K // 2), WL.random_bytes(2, N, K // 2)
