@@ -116,9 +116,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 // so that the compiler's waits for a stage's loads are exact; the loads of
 // step t + 2 are issued at the start of step t, into the stage step t - 2
 // used.  At the end of step t the wave waits for its own share of B step t + 1
-// (every vector-memory operation it issued after that share belongs to step t:
-// KS loads, KG at a group start, where the next group's exponents are loaded
-// too), then the workgroup barrier makes the whole stage visible.  The
+// (the last operation it issued before step t) by allowing only step t's own
+// KS operand loads to remain in flight, then the workgroup barrier makes the
+// whole stage visible.  At a group start the step also loads the next group's
+// exponents, ahead of its operand loads; they are older, so the same count
+// waits for them too, and it stays right where the compiler drops them (the
+// last group's are never used) or a wave skips the B exponents.  The
 // exponents of B (shared by every wave) go through a double-buffered LDS
 // table once per group.  A step past the end of K is loaded (harmlessly,
 // inside or past the operand's range) but not multiplied.
@@ -129,8 +132,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   constexpr int NT = NW * 64;
   static_assert(NW == 4 || NW == 8, "B: 16 or 32 rows per wave and step");
   constexpr int BPW = 128 / (16 * NW);      // B loads per wave and step
-  constexpr int KS = TM + BPW;              // vector-memory operations per step
-  constexpr int KG = KS + TM;               // ... at a group start (plus the A exponents)
+  constexpr int KS = TM + BPW;              // operand loads per step
   constexpr int BSTAGE = 128 * kRow;
   constexpr int ASTAGE = NW * TM * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t sa0[ASTAGE];
@@ -244,7 +246,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     compute(S0{}, sa0, sb0);          // step kt (always < nkt)
     __builtin_amdgcn_sched_barrier(0);
-    stage_barrier<KG>();
+    stage_barrier<KS>();
     issue(sa3, sb3, kt + 3);
     __builtin_amdgcn_sched_barrier(0);
     if (full || kt + 1 < nkt) compute(S1{}, sa1, sb1);
