@@ -129,7 +129,6 @@ template <int NW, int TM, int WPE>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   constexpr int BMD = NW * 16 * TM;
-  constexpr int NT = NW * 64;
   static_assert(NW == 4 || NW == 8, "B: 16 or 32 rows per wave and step");
   constexpr int BPW = 128 / (16 * NW);      // B loads per wave and step
   constexpr int KS = TM + BPW;              // operand loads per step
@@ -267,6 +266,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
   const int nfull = nkt / 4;
   for (int u = 0; u < nfull; ++u) group(u, std::true_type{});
   if (nfull < ngr) group(nfull, std::false_type{});
+  // the loads of the two steps past the last one are still writing this
+  // workgroup's LDS stages: let them land before the workgroup can end
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // epilogue: lane (fr, g) holds Y[m0 + wave*16*TM + 16 i + fr][n0 + 16 j +
   // 4 g + v] of block (i, j); pairs of blocks go out as full 128-byte rows
@@ -363,7 +365,7 @@ hipError_t launch_mx_gemm(const MxGemmParams& p, hipStream_t st) {
     // 256-row tiles of 8 waves (32 rows each) from one tile per CU up; fewer:
     // 64-row tiles of 4 waves, so that small shapes still spread over the CUs
     const int64_t grid = ((p.M + 255) / 256) * ((p.N + kBN - 1) / kBN);
-    W4A4_LAUNCH((mx_gemm_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+    W4A4_LAUNCH((mx_gemm_kernel<8, 2, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
   } else {
     const int64_t grid = ((p.M + 63) / 64) * ((p.N + kBN - 1) / kBN);
     W4A4_LAUNCH((mx_gemm_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);

@@ -22,7 +22,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "rotation_w4a4_quantization_amd", "csrc", "mx_gemm.hip")
 INSTANCES = {  # mangled name -> operand loads per step (A loads + B loads of one wave)
-    "_ZN4w4a414mx_gemm_kernelILi8ELi2ELi4EEEvNS_12MxGemmParamsE": 3,
+    "_ZN4w4a414mx_gemm_kernelILi8ELi2ELi2EEEvNS_12MxGemmParamsE": 3,
     "_ZN4w4a414mx_gemm_kernelILi4ELi1ELi2EEEvNS_12MxGemmParamsE": 3,
 }
 VMEM = re.compile(r"^\s*(buffer_load|buffer_store|buffer_atomic|global_load|global_store|global_atomic|"
