@@ -212,11 +212,13 @@ def test_mxfp4_gemm_rounding_bound(M, N, K):
     print(M, N, K, "rel_fro", r)
 
 
-@pytest.mark.parametrize("M,N,K,exact", [(2048, 4096, 384, True), (2048, 4096, 1152, False),
+@pytest.mark.parametrize("M,N,K,exact", [(2048, 4096, 256, True), (2048, 4096, 384, True),
+                                         (2048, 4096, 768, False), (2048, 4096, 1152, False),
                                          (2304, 4096, 640, False)])
 def test_mxfp4_gemm_one_tile_per_cu(M, N, K, exact):
     """The 256-row instance (one or more tiles per CU) over full groups of four
-    K-steps and a partial last group (K/128 = 3, 9, 5), checked on sampled rows
+    K-steps and partial last groups of 1, 2 and 3 steps (K/128 = 2, 3, 6, 9, 5),
+    checked on sampled rows
     that include the first and last row of every 256-row tile: exactly for
     K <= 384 with exponents in [-2, 2], else to the fp32 accumulation bound."""
     s = M + 3 * N + K
