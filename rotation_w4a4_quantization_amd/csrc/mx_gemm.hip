@@ -287,13 +287,17 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) mx_gemm_kernel(MxGemmParams p) {
 // ---------------------------------------------------------------- decode kernel (M <= 16)
 // The product is weight-bandwidth bound: one workgroup per 16 output
 // columns, its 4 waves splitting the K steps into contiguous ranges with 8
-// steps of loads in flight, partial sums added through LDS.  A lane takes the
-// exponents of 4 consecutive steps of its row in one 16-byte load and shifts
-// out the byte of its block g per step.  Rows of X beyond M read as zero
-// codes and exponents through the buffer range check; steps beyond K are not
-// multiplied (their exponent bytes belong to the next row).
+// steps of loads in flight, partial sums added through LDS.  The weight codes
+// go straight into each wave's LDS area with buffer_load_dwordx4 ... lds in the
+// coalesced order of the int8 decode kernel (lane 4 r + c' reads chunk
+// c' ^ ((r >> 2) & 3) of row r) and are read back in the MFMA lane layout.  A
+// lane takes the exponents of 4 consecutive steps of its row in one 16-byte
+// load and shifts out the byte of its block g per step.  Rows of X beyond M
+// read as zero codes and exponents through the buffer range check; steps
+// beyond K are not multiplied (their exponent bytes belong to the next row).
 __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
   __shared__ v4f red[3][64];
+  __shared__ __attribute__((aligned(16))) uint8_t sw[4][8 * 1024];   // [wave][step of the batch][16 rows x 64 B]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -308,12 +312,16 @@ __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
   const __amdgpu_buffer_rsrc_t rxe = rsrc(p.xe, p.M * lde);
   const __amdgpu_buffer_rsrc_t rwe = rsrc(p.we + n0 * lde, nw * lde);
   const int c_off = r * ldc + 16 * g;
+  const int lr = lane >> 2;
+  const int w_goff = lr * ldc + 16 * ((lane & 3) ^ ((lr >> 2) & 3));
+  const int w_roff = 64 * r + 16 * (g ^ ((r >> 2) & 3));
   const int e_off = r * lde;
   const int gshift = 8 * g;
+  uint8_t* const mine = sw[wave];
 
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t0 = 0; t0 < spw; t0 += 8) {
-    uint4 xa[8], wb[8], xe4[2], we4[2];
+    uint4 xa[8], xe4[2], we4[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kt = k_first + t0 + 4 * h;          // exponents of steps kt .. kt + 3
@@ -324,20 +332,25 @@ __global__ void __launch_bounds__(256) mx_gemm_decode_kernel(MxGemmParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int kt = k_first + t0 + u;
-      const int co = (t0 + u < spw && kt < nkt) ? c_off + kt * 64 : 0x7FFFFFF0;
-      wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, co, 0, 0));
-      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, co, 0, 0));
+      const bool in = t0 + u < spw && kt < nkt;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(mine + u * 1024), 16,
+                                               in ? w_goff + kt * 64 : 0x7FFFFFF0, 0, 0, 0);
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? c_off + kt * 64 : 0x7FFFFFF0, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int kt = k_first + t0 + u;
       if (t0 + u < spw && kt < nkt) {               // uniform over the wave
+        const uint4 wb = *reinterpret_cast<const uint4*>(mine + u * 1024 + w_roff);
         const uint4 xe = xe4[u >> 2], we = we4[u >> 2];
         const uint32_t xd = (u & 3) == 0 ? xe.x : (u & 3) == 1 ? xe.y : (u & 3) == 2 ? xe.z : xe.w;
         const uint32_t wd = (u & 3) == 0 ? we.x : (u & 3) == 1 ? we.y : (u & 3) == 2 ? we.z : we.w;
-        acc = mfma_mx<0>(xa[u], xd >> gshift, wb[u], wd >> gshift, acc);
+        acc = mfma_mx<0>(xa[u], xd >> gshift, wb, wd >> gshift, acc);
       }
     }
+    // every load of this batch has landed (its area is refilled next batch, and
+    // none may still be writing LDS when the workgroup ends)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
