@@ -33,6 +33,12 @@ namespace {
 
 constexpr int BN = 128, BK = 128;   // BK in 4-bit elements
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier for LDS traffic: this wave's LDS operations complete, then
+// s_barrier.  No memory fence, so loads still in flight (the next groups' A
+// codes on their way into LDS, B codes into registers) are not waited for;
+// each is waited for by the compiler where it is consumed.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr int LROW = 128;                      // LDS bytes per int8 row (one K step)
 
 // LDS layout of an int8 operand row: its eight 16-byte chunks are stored at
@@ -203,10 +209,16 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
 }
 
 // ---------------------------------------------------------------- A-direct kernel (asymmetric)
-// Same tiling and K-order convention as the symmetric A-direct kernel.
-// Activation codes are unsigned with one zero-point per (row, group of 128);
-// each wave widens its A rows straight to the int8 levels u - zp (|u - zp| <=
-// 15), so the MFMA accumulates 16 * A_g exactly; every group's sum is folded
+// Same tiling and K-order convention as the symmetric A-direct kernel, except
+// that each wave's A rows go from global memory straight into a per-wave LDS
+// stage with buffer_load_dwordx4 ... lds, in the coalesced order (lane 4 r + c'
+// reads chunk c' ^ ((r >> 2) & 3) of row r; the fragment reads in the MFMA
+// layout then hit distinct bank groups): loading the registers in the MFMA
+// layout directly, as the symmetric kernel does, makes this VALU-bound kernel
+// 10-14% slower on the gate/up shape.  Activation codes are unsigned with one
+// zero-point per (row, group of 128); each wave widens its A rows straight to
+// the int8 levels u - zp (|u - zp| <= 15), so the MFMA accumulates 16 * A_g
+// exactly; every group's sum is folded
 // into fp32 with that row's scale (block by block, inside the next group's
 // MFMA sequence), and the epilogue removes the factor 16 (exact) together
 // with the weight scale.  With the weight fragment first, the activation row
@@ -220,6 +232,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   constexpr int BSTAGE = 128 * LROW;
   constexpr int BMD = NW * 16 * TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[NW * TM * 1024];   // A stage of even groups, 1 KiB per 16 rows
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[NW * TM * 1024];   // ... of odd groups
   const bool b_stager = NT <= 512 || threadIdx.x < 512;
 
   const int tid = threadIdx.x;
@@ -247,7 +261,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
       (void*)(p.xs + m0 * G), (short)0, (int)(4 * zs_n < 0x7fffffff ? 4 * zs_n : 0x7fffffff), 0x00020000);
 
   const int fr = lane & 15, g = lane >> 4;
-  const int a_off = (wave * 16 * TM + fr) * (int)ldc + 16 * g;
+  const int alr = lane >> 2;
+  const int a_goff = (wave * 16 * TM + alr) * (int)ldc + 16 * ((lane & 3) ^ ((alr >> 2) & 3));
+  const int a_roff = wave * TM * 1024 + 64 * fr + 16 * (g ^ ((fr >> 2) & 3));
   int b_off[NCB], b_lds[NCB];
 #pragma unroll
   for (int j = 0; j < NCB; ++j) {
@@ -261,19 +277,20 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 #pragma unroll
   for (int i = 0; i < TM; ++i) arow[i] = (wave * 16 * TM + 16 * i + fr) * G;
 
-  // A codes, zero-points and scales of a group travel together in one of
-  // two register sets, loaded two groups ahead of their use (right after the
-  // step that emptied the set, so a whole step hides the load); all are
-  // buffer loads (no branches, so no wait is forced until the step that
-  // consumes them)
-  uint4 pa0[TM], pa1[TM], pb0[NCB], pb1[NCB];
+  // A codes of a group go into one of the two LDS stages, its zero-points and
+  // scales into the matching one of two register sets, two groups ahead of
+  // their use (right after the step that emptied the stage and the set, so a
+  // whole step hides the load); all are buffer loads (no branches, so no wait
+  // is forced until the step that consumes them)
+  uint4 pb0[NCB], pb1[NCB];
   uint32_t z0[TM], z1[TM];
   float s0[TM], s1[TM];
-  auto load_a = [&](uint4* pa, uint32_t* z, float* sx, int kt) {
+  auto load_a = [&](uint8_t* sa, uint32_t* z, float* sx, int kt) {
     const int kc = kt < nkt ? kt : nkt - 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      pa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + i * 16 * (int)ldc + kt * 64, 0, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + wave * TM * 1024 + i * 1024), 16,
+                                               a_goff + i * 16 * (int)ldc + kt * 64, 0, 0, 0);
       z[i] = __builtin_amdgcn_raw_buffer_load_b8(rz, arow[i] + kc, 0, 0);
       sx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (arow[i] + kc), 0, 0));
     }
@@ -336,7 +353,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   // compiler hoists every fold above the first MFMA of the group (the waves
   // of a SIMD then run VALU-only and MFMA-only phases in lockstep) and
   // spills; pinned, the group runs 3-10% faster with 202 VGPRs.
-  auto step = [&](const uint4* pa, const uint32_t* z, const float* sprev, int stage) {
+  auto step = [&](const uint8_t* sa, const uint32_t* z, const float* sprev, int stage) {
+    uint4 pa[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) pa[i] = *reinterpret_cast<const uint4*>(sa + a_roff + i * 1024);
     const uint8_t* Bs = smem + stage * BSTAGE;
     v4i bq0[3], bq1[3];
     bq0[0] = *reinterpret_cast<const v4i*>(Bs + bf0);
@@ -377,41 +397,45 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
       for (int j = 0; j < 8; ++j) fold(i, j, sf[i]);
   };
 
-  // Group g's codes, zero-points and scales sit in register set g & 1.
+  // Group g's codes sit in LDS stage g & 1, its zero-points and scales in
+  // register set g & 1.
   // Group g's step folds group g-1 with the scales held in sp; after the
   // step, sp takes group g's scales and set g & 1 is refilled with group
   // g+2.  sp starts at zero.
   float sp[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) sp[i] = 0.0f;
-  load_a(pa0, z0, s0, 0);
-  load_a(pa1, z1, s1, 1);
+  load_a(sa0, z0, s0, 0);
+  load_a(sa1, z1, s1, 1);
   load_b(pb0, 0);
   load_b(pb1, 1);
   store_b(pb0, 0);
-  __syncthreads();
+  lds_barrier();
   for (int kt = 0; kt + 1 < nkt; kt += 2) {
     load_b(pb0, kt + 2);
-    step(pa0, z0, sp, 0);             // group kt; fold of group kt - 1
+    step(sa0, z0, sp, 0);             // group kt; fold of group kt - 1
 #pragma unroll
     for (int i = 0; i < TM; ++i) sp[i] = s0[i];
-    load_a(pa0, z0, s0, kt + 2);
+    load_a(sa0, z0, s0, kt + 2);
     store_b(pb1, 1);
-    __syncthreads();
+    lds_barrier();
     load_b(pb1, kt + 3);
-    step(pa1, z1, sp, 1);             // group kt + 1; fold of group kt
+    step(sa1, z1, sp, 1);             // group kt + 1; fold of group kt
 #pragma unroll
     for (int i = 0; i < TM; ++i) sp[i] = s1[i];
-    load_a(pa1, z1, s1, kt + 3);
+    load_a(sa1, z1, s1, kt + 3);
     store_b(pb0, 0);
-    __syncthreads();
+    lds_barrier();
   }
   if (nkt & 1) {
-    step(pa0, z0, sp, 0);             // group nkt - 1; fold of group nkt - 2
+    step(sa0, z0, sp, 0);             // group nkt - 1; fold of group nkt - 2
     fold_all(s0);
   } else {
     fold_all(sp);                     // group nkt - 1
   }
+  // the A loads of the two groups past the last one are still writing this
+  // wave's LDS stages: let them land before the workgroup can end
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // the accumulators hold 16 x the levels' products: the exact power-of-two
   // factor is removed here, once, with the weight scale
