@@ -112,6 +112,27 @@ def test_rotate_quant_empty():
     assert c.shape == (0, 128) and s.shape == (0,)
 
 
+def test_empty_batches_are_no_ops():
+    """Zero rows (M = 0, N = 0, S = 0, B = 0) return OK and launch nothing,
+    symmetric and asymmetric, through every quantize and GEMM entry point."""
+    c, s, z = R.rotate_quant_act(torch.empty((0, 256), dtype=torch.float16, device="cuda"), 128, act_mode="asym")
+    assert c.shape == (0, 128) and s.shape == (0, 2) and z.shape == (0, 2)
+    wc, ws, wg = R.quant_weight_offline(torch.empty((0, 256), dtype=torch.float16, device="cuda"), 128)
+    assert wc.shape == (0, 128) and ws.shape == (0,) and wg.shape == (0, 2)
+    for B, H, S in ((0, 4, 16), (2, 0, 16), (2, 4, 0)):
+        kc, ks, kz = R.kv_rotate_quant4(torch.empty((B, H, S, 128), dtype=torch.float16, device="cuda"))
+        assert kc.shape == (B, H, S, 64) and ks.shape == (B, H, S) and kz.shape == (B, H, S)
+    w = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    one = torch.ones((8,), dtype=torch.float32, device="cuda")
+    xc = torch.empty((0, 128), dtype=torch.uint8, device="cuda")
+    y = R.w4a4_gemm(xc, torch.empty((0,), dtype=torch.float32, device="cuda"), None, w, one)
+    assert y.shape == (0, 8)
+    y = R.w4a4_gemm(xc, torch.empty((0, 2), dtype=torch.float32, device="cuda"),
+                    torch.empty((0, 2), dtype=torch.uint8, device="cuda"), w, one, act_mode="asym")
+    assert y.shape == (0, 8)
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- asymmetric activations and KV
 @pytest.mark.parametrize("M,K", [(256, 8192), (1, 128), (37, 384), (300, 2176)])
 def test_rotate_quant_asym(M, K):
