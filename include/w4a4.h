@@ -24,6 +24,11 @@
  *  - Every call is asynchronous and ordered on `stream` (a hipStream_t;
  *    NULL means the null stream).  Buffers must stay alive until the stream
  *    work completes.  Outputs must not alias inputs.
+ *  - A call enqueues kernel launches only: no memset, copy, allocation or
+ *    host synchronization.  A sequence of calls can therefore be captured
+ *    into a HIP graph and replayed (the device must have been used by one
+ *    uncaptured call first, for the architecture check).  A replay reads
+ *    the captured pointers, so new data goes into the same buffers.
  *  - Arguments are validated on the host before anything is enqueued; on
  *    any error nothing is launched, outputs are untouched, the status says
  *    why and w4a4_last_error() holds a message.  A failed launch returns
