@@ -532,6 +532,11 @@ def main() -> int:
                                      "GB/s": round(w_gbs, 1),
                                      "frac_hbm_peak": round(w_gbs / HBM_PEAK_GBS, 4), "bytes": w_bytes},
         },
+        # the online part of the layer alone (activation rotate+quant, then the
+        # GEMM; the weights quantized once, offline): 2MNK over the sum of the
+        # two kernels' device durations, without the gaps between launches
+        "online_layer": {"ms": round(kt["rotate_quant_act"] + kt["w4a4_gemm"], 5),
+                         "TOPS": round(ops / ((kt["rotate_quant_act"] + kt["w4a4_gemm"]) * 1e-3) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

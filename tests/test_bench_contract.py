@@ -57,6 +57,10 @@ def test_bench_line_fields():
     M, N, K = d["config"]["M"], d["config"]["N"], d["config"]["K"]
     assert abs(d["value"] - 2 * M * N * K / (d["ms_per_step"] * 1e-3) / 1e12) / d["value"] < 0.01
     assert d["value"] < rf["achieved"]
+    # the online layer (activation rotate+quant + GEMM) sits between the two
+    ol = d["online_layer"]
+    assert d["value"] < ol["TOPS"] < rf["achieved"]
+    assert abs(ol["ms"] - d["kernels"]["rotate_quant_act"]["avg_ms"] - d["kernels"]["w4a4_gemm"]["avg_ms"]) < 1e-4
 
 
 def test_committed_gemm_profile_gives_the_traffic_figure():
