@@ -76,7 +76,7 @@ w4a4_status check_device() {
       return verdict(W4A4_ERR_DEVICE, m);
     }
     if (w4a4::gemm_prepare_device() != hipSuccess)
-      return fail(W4A4_ERR_DEVICE, "could not raise the LDS limit of the GEMM kernels");
+      return fail(W4A4_ERR_DEVICE, "GEMM set-up failed on device %d", dev);
     void* ptr = nullptr;
     const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e != hipSuccess || ptr == nullptr)
