@@ -5,7 +5,8 @@
 // Friends", sections "A rotation changes nothing, and that is the point" and
 // "What it buys in 4 bits").  CDNA4 has no INT4 matrix instruction, so the
 // packed nibbles are widened to int8 and multiplied with
-// v_mfma_i32_16x16x64_i8 into an exact int32 accumulator.
+// v_mfma_i32_16x16x64_i8 (v_mfma_i32_32x32x32_i8 in the asymmetric kernel
+// for large shapes) into an exact int32 accumulator.
 //
 // Widening (no per-element shifts): for a dword of 8 two's-complement
 // nibbles p, the bytes of (p & 0xF0F0F0F0) are 16 * (odd nibbles) and the
@@ -49,6 +50,16 @@ constexpr int LROW = 128;                      // LDS bytes per int8 row (one K 
 // 16-byte padding or a (row >> 1) swizzle.
 __device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_chunk(int row, int c) { return row * LROW + ((c ^ lds_swz(row)) << 4); }
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ v16i mfma32(const v4i& a, const v4i& b, const v16i& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 
 }  // namespace
 
@@ -223,7 +234,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
 // MFMA sequence), and the epilogue removes the factor 16 (exact) together
 // with the weight scale.  With the weight fragment first, the activation row
 // a lane widens is also the output row it accumulates, so one zero-point
-// and one scale per row block and group serve each lane.
+// and one scale per row block and group serve each lane.  Used for the
+// 128-row tiles of shapes with fewer than 256 tiles of 256 rows; larger
+// shapes take gemm_asym_x32_kernel below.
 template <int NW, int TM, int WPE>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmParams p) {
@@ -462,6 +475,263 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
   }
 }
 
+// ---------------------------------------------------------------- asymmetric kernel, 32x32x32 blocks
+// 256 x 128 output tile, 8 waves of 32 rows x 128 columns, each wave's tile
+// as four 32x32 blocks of v_mfma_i32_32x32x32_i8.  With the weight fragment
+// first, lane (h, r) = (lane >> 5, lane & 31) accumulates activation row r
+// and weight columns 8 s + 4 h + v (s, v = 0..3) of each block, so one
+// zero-point and one scale per lane and group serve all its 64 outputs.
+// The kernel is bound by VALU issue: each output and group costs a convert
+// and an fma of the fold, and widening the A codes to u - zp costs 14
+// instructions per 32 K values of a row; one 32x32x32 MFMA hides about
+// twice as many VALU instructions as the two 16x16x64 MFMAs doing the same
+// work (32 against 16 issue cycles).
+//
+// Per group g (128 K values: a 64-byte packed segment of every row):
+// - A: each wave's 32 rows go from global memory into its own LDS stage
+//   (g & 1) with buffer_load_dwordx4 ... lds, row R's chunk c at
+//   64 R + 16 (c ^ ((R >> 2) & 3)).  Lane (h, r) reads chunks 2h and 2h + 1
+//   of row r; quarter q (K values 32 q .. 32 q + 31 of the fragment order)
+//   widens dwords 2 (q & 1) and 2 (q & 1) + 1 of chunk 2h + (q >> 1).  Group
+//   g + 2's codes are requested into the stage as soon as group g's are in
+//   registers, a whole step ahead of their use.
+// - B: int8 weight rows in LDS as in the other kernels; quarter q's fragment
+//   of lane (h, r) is chunk 4h + q of row r, which is the same K order as
+//   A's widening.  Four stages, filled two groups at a time, so one
+//   workgroup barrier serves two groups.
+// - Order inside a group: block c's four MFMAs run back to back with the
+//   fold of block c + 1's previous group (during block 3: block 0's group g)
+//   spread over them, 8 VALU instructions after each MFMA; block c + 1's
+//   weight fragments are read during block c.  After the last group, blocks
+//   1..3 are folded once more.
+// The fold order per output (group 0, 1, ...) and the epilogue are those of
+// gemm_adirect_asym_kernel, so both kernels give identical results.
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
+  constexpr int BMD = 256;
+  constexpr int BSTAGE = 128 * LROW;                // one B stage: 128 rows x 128 int8
+  constexpr int ASTAGE = 8 * 2048;                  // one A stage: 8 waves x 32 rows x 64 packed bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * BSTAGE + 2 * ASTAGE];
+  uint8_t* const sa0 = lds + 4 * BSTAGE;
+  uint8_t* const sa1 = sa0 + ASTAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
+  int64_t tm, tn;
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BMD, n0 = tn * BN;
+  const int nkt = p.K / BK;
+  const int G = nkt;
+  const int64_t ldc = p.K / 2;
+
+  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
+  // per-(row, group) zero-points and scales of this tile's rows; rows past M read as 0
+  const int64_t zs_n = (p.M - m0) * G;
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xz + m0 * G), (short)0, (int)(zs_n < 0x7fffffff ? zs_n : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xs + m0 * G), (short)0, (int)(4 * zs_n < 0x7fffffff ? 4 * zs_n : 0x7fffffff), 0x00020000);
+
+  const int h = lane >> 5, r = lane & 31;
+  const int alr = lane >> 2;                        // DMA: lane 4 R + c' carries chunk c' ^ ((R >> 2) & 3) of row R
+  const int a_goff = (wave * 32 + alr) * (int)ldc + 16 * ((lane & 3) ^ ((alr >> 2) & 3));
+  const int a_roff0 = wave * 2048 + 64 * r + 16 * ((2 * h) ^ ((r >> 2) & 3));
+  const int a_roff1 = wave * 2048 + 64 * r + 16 * ((2 * h + 1) ^ ((r >> 2) & 3));
+  const int b_off = (tid >> 2) * (int)ldc + 16 * (tid & 3);   // B staging: row tid >> 2, packed chunk tid & 3
+  const int b_lds = lds_chunk(tid >> 2, 2 * (tid & 3));
+  int bfq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bfq[q] = lds_chunk(r, 4 * h + q);
+  const int arow = (wave * 32 + r) * G;
+
+  auto load_dma = [&](uint8_t* sa, int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + wave * 2048 + i * 1024), 16,
+                                               a_goff + i * 16 * (int)ldc + kt * 64, 0, 0, 0);
+  };
+  auto load_zs = [&](uint32_t& z, float& sx, int kt) {
+    const int kc = kt < nkt ? kt : nkt - 1;
+    z = __builtin_amdgcn_raw_buffer_load_b8(rz, arow + kc, 0, 0);
+    sx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (arow + kc), 0, 0));
+  };
+  auto load_b = [&](uint4& pb, int kt) {
+    pb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4& pb, int stage) {
+    uint8_t* base = lds + stage * BSTAGE;
+    const uint32_t w[4] = {pb.x, pb.y, pb.z, pb.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+    *reinterpret_cast<uint4*>(base + b_lds) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(base + (b_lds ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+  };
+
+  v16i acc[4];
+  float yf[4][16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc[c][e] = 0;
+      yf[c][e] = 0.0f;
+    }
+  // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
+  auto widen_q = [&](uint32_t d0, uint32_t d1, uint32_t z) -> v4i {
+    const uint32_t bias = (128u - z) * 0x01010101u;
+    const uint32_t o0 = ((d0 & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+    const uint32_t o1 = (((d0 >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+    const uint32_t o2 = ((d1 & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+    const uint32_t o3 = (((d1 >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
+    return v4i{(int)o0, (int)o1, (int)o2, (int)o3};
+  };
+  const v16i zero16 = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+  // One group: A codes from stage sa, B rows from stage bst, zero-point z,
+  // scales of this group (s_cur) and the previous one (s_prev).
+  auto step = [&](uint8_t* sa, uint32_t z, float s_cur, float s_prev, int bst, int next_kt) {
+    // The wait for this group's A codes (written into LDS, which the
+    // compiler does not reliably track) is explicit.  Vector-memory
+    // operations complete in order, and the ones issued after this group's
+    // codes, zero-point and scale are B rows of two groups (2), the next
+    // group's codes (2) and its zero-point and scale (2), in one order or
+    // another, so vmcnt(6) leaves the codes landed.  (A CPU test walks the
+    // compiled code's paths for this.)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    const uint4 pa0 = *reinterpret_cast<const uint4*>(sa + a_roff0);
+    const uint4 pa1 = *reinterpret_cast<const uint4*>(sa + a_roff1);
+    const uint8_t* Bs = lds + bst * BSTAGE;
+    v4i a[4];
+    a[0] = widen_q(pa0.x, pa0.y, z);
+    a[1] = widen_q(pa0.z, pa0.w, z);
+    a[2] = widen_q(pa1.x, pa1.y, z);
+    a[3] = widen_q(pa1.z, pa1.w, z);
+    // the stage has been read (the widened values exist) before group
+    // next_kt's codes are requested into it
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+    load_dma(sa, next_kt);
+    __builtin_amdgcn_sched_barrier(0);
+    v4i bb[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bb[0][q] = *reinterpret_cast<const v4i*>(Bs + bfq[q]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bb[(c + 1) & 1][q] = *reinterpret_cast<const v4i*>(Bs + (c + 1) * 32 * LROW + bfq[q]);
+      }
+      const int fc = (c + 1) & 3;
+      const float sf = c < 3 ? s_prev : s_cur;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[c] = mfma32(bb[c & 1][q], a[q], q == 0 ? zero16 : acc[c]);
+#pragma unroll
+        for (int e = 4 * q; e < 4 * q + 4; ++e) yf[fc][e] = fmaf(sf, (float)acc[fc][e], yf[fc][e]);
+        // pinned: left to itself the compiler gathers the folds away from
+        // the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Group g: A codes in stage g & 1, B rows in stage g & 3, zero-point in
+  // z[g & 1], scale in s[g & 3].  A scale is used by its own step and the
+  // next one and is loaded two groups ahead, so four slots rotate with no
+  // register copies (a copy would wait for the load at once).
+  uint32_t z[2];
+  float s[4];
+  s[3] = 0.0f;                                      // group "-1": the first step's folds add 0 * 0
+  load_dma(sa0, 0);
+  load_zs(z[0], s[0], 0);
+  load_dma(sa1, 1);
+  load_zs(z[1], s[1], 1);
+  uint4 pb0, pb1;
+  load_b(pb0, 0);
+  load_b(pb1, 1);
+  store_b(pb0, 0);
+  store_b(pb1, 1);
+  lds_barrier();
+  // groups kt and kt + 1 (kt = 0 or 2 mod 4); B rows of kt + 2 and kt + 3
+  // are loaded meanwhile and staged after both steps
+  auto pair = [&](int kt, auto J, bool two) {
+    constexpr int j = decltype(J)::value;
+    load_b(pb0, kt + 2);
+    load_b(pb1, kt + 3);
+    step(sa0, z[0], s[j], s[(j + 3) & 3], j, kt + 2);
+    load_zs(z[0], s[(j + 2) & 3], kt + 2);
+    if (two) {
+      step(sa1, z[1], s[j + 1], s[j], j + 1, kt + 3);
+      load_zs(z[1], s[(j + 3) & 3], kt + 3);
+    }
+    store_b(pb0, (j + 2) & 3);
+    store_b(pb1, (j + 3) & 3);
+    lds_barrier();
+  };
+  int kt = 0;
+  for (; kt + 3 < nkt; kt += 4) {
+    pair(kt, IntTag<0>{}, true);
+    pair(kt + 2, IntTag<2>{}, true);
+  }
+  if (kt < nkt) pair(kt, IntTag<0>{}, kt + 1 < nkt);
+  if (kt + 2 < nkt) pair(kt + 2, IntTag<2>{}, kt + 3 < nkt);
+  // blocks 1..3 still hold the last group
+  const int jl = (nkt - 1) & 3;
+  const float sl = jl == 0 ? s[0] : jl == 1 ? s[1] : jl == 2 ? s[2] : s[3];
+#pragma unroll
+  for (int c = 1; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) yf[c][e] = fmaf(sl, (float)acc[c][e], yf[c][e]);
+  // the A codes requested past the last group are still writing the stages
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                                  // the B stages become the epilogue areas
+
+  // Epilogue: each 32 x 32 block goes through a 4 KiB LDS area of the wave
+  // (rows of 128 bytes, chunk c of row R at c ^ s(R)) to full-line stores;
+  // the accumulators hold 16 x the levels' products, removed here, once,
+  // with the weight scale.
+  uint8_t* ew = lds + wave * 32 * LROW;
+  const int64_t mw = m0 + wave * 32;
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + n0), (short)0, (int)((p.N - n0) * 4 < 0x7fffffff ? (p.N - n0) * 4 : 0x7fffffff), 0x00020000);
+  const int eu = lane & 7, er = lane >> 3;
+  const bool ld_ok = (p.ldy & 3) == 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const v4f swc = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (32 * c + 4 * eu), 0, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<v4f*>(ew + r * LROW + 16 * ((2 * q + h) ^ lds_swz(r))) =
+          v4f{yf[c][4 * q], yf[c][4 * q + 1], yf[c][4 * q + 2], yf[c][4 * q + 3]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = er + 8 * q;
+      const v4f av = *reinterpret_cast<const v4f*>(ew + rr * LROW + 16 * (eu ^ lds_swz(rr)));
+      v4f yv;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yv[v] = av[v] * (swc[v] * 0.0625f);
+      const int64_t row = mw + rr;
+      const int64_t col = n0 + 32 * c + 4 * eu;
+      if (ld_ok && row < p.M && col + 4 <= p.N) {
+        __builtin_nontemporal_store(yv, reinterpret_cast<v4f*>(p.y + row * p.ldy + col));
+      } else if (row < p.M) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (col + v < p.N) p.y[row * p.ldy + col + v] = yv[v];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // ---------------------------------------------------------------- decode kernel
 // M <= 16 rows (symmetric): one workgroup per 16 output columns; the 4 waves
 // split the 128-wide K steps (wave w takes steps w, w+4, ...).  The kernel is
@@ -568,14 +838,15 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  // asymmetric per-group activations: 256-row tiles of 8 waves (32 x 128
-  // each) from one tile per CU up (gate/up 8192 x 28672 x 8192: 2.74 ms
-  // against 3.1 ms for 16-row wave tiles), else 128-row tiles of 8 waves
-  // (16 x 128 each) so that small shapes still spread over the CUs
+  // asymmetric per-group activations: 256-row tiles of 8 waves with 32x32
+  // MFMA blocks from one tile per CU up (gate/up 8192 x 28672 x 8192:
+  // 2.44-2.50 ms against 2.60-2.62 ms for the 16x16x64 kernel's 256-row
+  // instance on the same boxes), else 128-row tiles of 8 waves (16 x 128
+  // each) so that small shapes still spread over the CUs
   const int64_t tiles_n = (p.N + BN - 1) / BN;
   const int64_t grid = ((p.M + 255) / 256) * tiles_n;
   if (grid >= 256) {
-    W4A4_LAUNCH((gemm_adirect_asym_kernel<8, 2, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+    W4A4_LAUNCH(gemm_asym_x32_kernel, dim3((uint32_t)grid), dim3(512), 0, st, p);
   } else {
     const int64_t grid = ((p.M + 127) / 128) * tiles_n;
     W4A4_LAUNCH((gemm_adirect_asym_kernel<8, 1, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);

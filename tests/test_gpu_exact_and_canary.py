@@ -112,6 +112,35 @@ def test_gemm_asym_same_codes_256_row_instance(M, N, K):
     assert err < 1e-6
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 4000, 128), (2000, 4000, 256), (2000, 4000, 384),
+                                   (1100, 7700, 640), (2048, 4096, 1280), (1100, 7700, 1408)])
+def test_gemm_asym_x32_group_counts_exact(M, N, K):
+    """The 256-row asymmetric kernel (32x32 MFMA blocks, groups processed in
+    pairs of a four-group loop) over 1, 2, 3, 5, 10 and 11 groups, with M and
+    N not multiples of the tile: unit scales give the oracle's integers
+    exactly."""
+    u, zp, qw = _asym_case(M, N, K, M + N + K)
+    G = K // 128
+    y = host(R.w4a4_gemm(dev(O.pack_nibbles(u)), dev(np.ones((M, G), np.float32)), dev(zp.astype(np.uint8)),
+                         dev(O.pack_nibbles(qw)), dev(np.ones(N, np.float32)), act_mode="asym"))
+    lv = u.reshape(M, G, 128) - zp[:, :, None]
+    want = O.int_gemm(lv.reshape(M, K), qw)
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1100, 7700, 1408), (2000, 4000, 384)])
+def test_gemm_asym_x32_random_scales(M, N, K):
+    """Random per-group scales through the same kernel: within 1e-6 of the
+    oracle's float64 sum of group products."""
+    u, zp, qw = _asym_case(M, N, K, 5 * M + K)
+    rng = np.random.default_rng(M + K)
+    sx = (rng.random((M, K // 128)) + 0.05).astype(np.float32)
+    sw = (rng.random(N) * 0.01 + 1e-4).astype(np.float32)
+    y = host(R.w4a4_gemm(dev(O.pack_nibbles(u)), dev(sx), dev(zp.astype(np.uint8)), dev(O.pack_nibbles(qw)),
+                         dev(sw), act_mode="asym"))
+    assert rel_fro(y, O.gemm_asym_f64(u, zp, sx, qw, sw)) < 1e-6
+
+
 # ---------------------------------------------------------------- canaries after every output
 CANARY = 0xA5
 TAIL = 256
