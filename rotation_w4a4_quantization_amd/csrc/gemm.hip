@@ -5,8 +5,8 @@
 // Friends", sections "A rotation changes nothing, and that is the point" and
 // "What it buys in 4 bits").  CDNA4 has no INT4 matrix instruction, so the
 // packed nibbles are widened to int8 and multiplied with
-// v_mfma_i32_16x16x64_i8 (v_mfma_i32_32x32x32_i8 in the asymmetric kernel
-// for large shapes) into an exact int32 accumulator.
+// v_mfma_i32_16x16x64_i8 (v_mfma_i32_32x32x32_i8 in the asymmetric kernel)
+// into an exact int32 accumulator.
 //
 // Widening (no per-element shifts): for a dword of 8 two's-complement
 // nibbles p, the bytes of (p & 0xF0F0F0F0) are 16 * (odd nibbles) and the
@@ -219,264 +219,15 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_kernel(GemmParams p)
   }
 }
 
-// ---------------------------------------------------------------- A-direct kernel (asymmetric)
-// Same tiling and K-order convention as the symmetric A-direct kernel, except
-// that each wave's A rows go from global memory straight into a per-wave LDS
-// stage with buffer_load_dwordx4 ... lds, in the coalesced order (lane 4 r + c'
-// reads chunk c' ^ ((r >> 2) & 3) of row r; the fragment reads in the MFMA
-// layout then hit distinct bank groups): loading the registers in the MFMA
-// layout directly, as the symmetric kernel does, makes this VALU-bound kernel
-// 10-14% slower on the gate/up shape.  Activation codes are unsigned with one
-// zero-point per (row, group of 128); each wave widens its A rows straight to
-// the int8 levels u - zp (|u - zp| <= 15), so the MFMA accumulates 16 * A_g
-// exactly; every group's sum is folded
-// into fp32 with that row's scale (block by block, inside the next group's
-// MFMA sequence), and the epilogue removes the factor 16 (exact) together
-// with the weight scale.  With the weight fragment first, the activation row
-// a lane widens is also the output row it accumulates, so one zero-point
-// and one scale per row block and group serve each lane.  Used for the
-// 128-row tiles of shapes with fewer than 256 tiles of 256 rows; larger
-// shapes take gemm_asym_x32_kernel below.
-template <int NW, int TM, int WPE>
-__global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int NCB = NT >= 512 ? 1 : 512 / NT;
-  constexpr int BSTAGE = 128 * LROW;
-  constexpr int BMD = NW * 16 * TM;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BSTAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[NW * TM * 1024];   // A stage of even groups, 1 KiB per 16 rows
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[NW * TM * 1024];   // ... of odd groups
-  const bool b_stager = NT <= 512 || threadIdx.x < 512;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
-  int64_t tm, tn;
-  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * BMD, n0 = tn * BN;
-  const int nkt = p.K / BK;
-  const int G = nkt;
-  const int64_t ldc = p.K / 2;
-
-  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
-  // per-(row, group) zero-points and scales of this tile's rows; rows past M read as 0
-  const int64_t zs_n = (p.M - m0) * G;
-  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.xz + m0 * G), (short)0, (int)(zs_n < 0x7fffffff ? zs_n : 0x7fffffff), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.xs + m0 * G), (short)0, (int)(4 * zs_n < 0x7fffffff ? 4 * zs_n : 0x7fffffff), 0x00020000);
-
-  const int fr = lane & 15, g = lane >> 4;
-  const int alr = lane >> 2;
-  const int a_goff = (wave * 16 * TM + alr) * (int)ldc + 16 * ((lane & 3) ^ ((alr >> 2) & 3));
-  const int a_roff = wave * TM * 1024 + 64 * fr + 16 * (g ^ ((fr >> 2) & 3));
-  int b_off[NCB], b_lds[NCB];
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) {
-    const int cb = tid + NT * j;
-    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
-    b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
-  }
-  const int bf0 = lds_chunk(fr, 2 * g), bf1 = lds_chunk(fr, 2 * g + 1);
-  // the activation row a lane widens and accumulates, as an offset into [rows][G]
-  int arow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) arow[i] = (wave * 16 * TM + 16 * i + fr) * G;
-
-  // A codes of a group go into one of the two LDS stages, its zero-points and
-  // scales into the matching one of two register sets, two groups ahead of
-  // their use (right after the step that emptied the stage and the set, so a
-  // whole step hides the load); all are buffer loads (no branches, so no wait
-  // is forced until the step that consumes them)
-  uint4 pb0[NCB], pb1[NCB];
-  uint32_t z0[TM], z1[TM];
-  float s0[TM], s1[TM];
-  auto load_a = [&](uint8_t* sa, uint32_t* z, float* sx, int kt) {
-    const int kc = kt < nkt ? kt : nkt - 1;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + wave * TM * 1024 + i * 1024), 16,
-                                               a_goff + i * 16 * (int)ldc + kt * 64, 0, 0, 0);
-      z[i] = __builtin_amdgcn_raw_buffer_load_b8(rz, arow[i] + kc, 0, 0);
-      sx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (arow[i] + kc), 0, 0));
-    }
-  };
-  auto load_b = [&](uint4* pb, int kt) {
-    if (!b_stager) return;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j)
-      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
-  };
-  auto store_b = [&](const uint4* pb, int stage) {
-    if (!b_stager) return;
-    uint8_t* base = smem + stage * BSTAGE;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
-      *reinterpret_cast<uint4*>(base + b_lds[j]) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(base + (b_lds[j] ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-  };
-
-  // One accumulator set: during group g's step, block (i, j)'s group g-1
-  // result is folded into fp32 right before group g's MFMAs overwrite it.
-  // Before the first group the accumulators and the scales are zero, so that
-  // first fold adds exactly 0.
-  v4i acc[TM][8];
-  float yf[TM][8][4];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[i][j] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) yf[i][j][v] = 0.0f;
-    }
-  // byte-wise u - zp without cross-byte carries: (u + 128 - zp) ^ 0x80
-  auto widen_row = [&](const uint4& pa, uint32_t z, v4i& a0, v4i& a1) {
-    const uint32_t bias = (128u - z) * 0x01010101u;
-    const uint32_t w[4] = {pa.x, pa.y, pa.z, pa.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      o[2 * d] = ((w[d] & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
-      o[2 * d + 1] = (((w[d] >> 4) & 0x0F0F0F0Fu) + bias) ^ 0x80808080u;
-    }
-    a0 = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    a1 = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-  };
-  auto fold = [&](int i, int j, float sp) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) yf[i][j][v] = fmaf(sp, (float)acc[i][j][v], yf[i][j][v]);
-  };
-  // One group: B fragments are read two block columns ahead, and in every
-  // block column the fold of each row block sits between MFMAs (the second
-  // MFMA of a block's chain comes after the first MFMA of the other row
-  // blocks).  sched_barrier fences pin that order: left to itself the
-  // compiler hoists every fold above the first MFMA of the group (the waves
-  // of a SIMD then run VALU-only and MFMA-only phases in lockstep) and
-  // spills; pinned, the group runs 3-10% faster with 202 VGPRs.
-  auto step = [&](const uint8_t* sa, const uint32_t* z, const float* sprev, int stage) {
-    uint4 pa[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) pa[i] = *reinterpret_cast<const uint4*>(sa + a_roff + i * 1024);
-    const uint8_t* Bs = smem + stage * BSTAGE;
-    v4i bq0[3], bq1[3];
-    bq0[0] = *reinterpret_cast<const v4i*>(Bs + bf0);
-    bq1[0] = *reinterpret_cast<const v4i*>(Bs + bf1);
-    bq0[1] = *reinterpret_cast<const v4i*>(Bs + 16 * LROW + bf0);
-    bq1[1] = *reinterpret_cast<const v4i*>(Bs + 16 * LROW + bf1);
-    v4i a[TM][2];
-    widen_row(pa[0], z[0], a[0][0], a[0][1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const v4i b0 = bq0[j % 3], b1 = bq1[j % 3];
-      if (j + 2 < 8) {
-        bq0[(j + 2) % 3] = *reinterpret_cast<const v4i*>(Bs + (j + 2) * 16 * LROW + bf0);
-        bq1[(j + 2) % 3] = *reinterpret_cast<const v4i*>(Bs + (j + 2) * 16 * LROW + bf1);
-      }
-      fold(0, j, sprev[0]);
-      v4i t[TM];
-      t[0] = mfma16(b0, a[0][0], v4i{0, 0, 0, 0});
-      if (j == 0) {
-#pragma unroll
-        for (int i = 1; i < TM; ++i) widen_row(pa[i], z[i], a[i][0], a[i][1]);
-      }
-#pragma unroll
-      for (int i = 1; i < TM; ++i) {
-        fold(i, j, sprev[i]);
-        t[i] = mfma16(b0, a[i][0], v4i{0, 0, 0, 0});
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][j] = mfma16(b1, a[i][1], t[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto fold_all = [&](const float* sf) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fold(i, j, sf[i]);
-  };
-
-  // Group g's codes sit in LDS stage g & 1, its zero-points and scales in
-  // register set g & 1.
-  // Group g's step folds group g-1 with the scales held in sp; after the
-  // step, sp takes group g's scales and set g & 1 is refilled with group
-  // g+2.  sp starts at zero.
-  float sp[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) sp[i] = 0.0f;
-  load_a(sa0, z0, s0, 0);
-  load_a(sa1, z1, s1, 1);
-  load_b(pb0, 0);
-  load_b(pb1, 1);
-  store_b(pb0, 0);
-  lds_barrier();
-  for (int kt = 0; kt + 1 < nkt; kt += 2) {
-    load_b(pb0, kt + 2);
-    step(sa0, z0, sp, 0);             // group kt; fold of group kt - 1
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sp[i] = s0[i];
-    load_a(sa0, z0, s0, kt + 2);
-    store_b(pb1, 1);
-    lds_barrier();
-    load_b(pb1, kt + 3);
-    step(sa1, z1, sp, 1);             // group kt + 1; fold of group kt
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sp[i] = s1[i];
-    load_a(sa1, z1, s1, kt + 3);
-    store_b(pb0, 0);
-    lds_barrier();
-  }
-  if (nkt & 1) {
-    step(sa0, z0, sp, 0);             // group nkt - 1; fold of group nkt - 2
-    fold_all(s0);
-  } else {
-    fold_all(sp);                     // group nkt - 1
-  }
-  // the A loads of the two groups past the last one are still writing this
-  // wave's LDS stages: let them land before the workgroup can end
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // the accumulators hold 16 x the levels' products: the exact power-of-two
-  // factor is removed here, once, with the weight scale
-  const int64_t mw = m0 + wave * 16 * TM;
-  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.ws + n0), (short)0, (int)((p.N - n0) * 4 < 0x7fffffff ? (p.N - n0) * 4 : 0x7fffffff), 0x00020000);
-  const bool ld_ok = (p.ldy & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t r0 = mw + 16 * i;
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const v4f swa = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 4 * g), 0, 0));
-      const v4f swb = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (16 * j + 16 + 4 * g), 0, 0));
-      v4f ya, yb;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        ya[v] = yf[i][j][v] * (swa[v] * 0.0625f);
-        yb[v] = yf[i][j + 1][v] * (swb[v] * 0.0625f);
-      }
-      const bool full = ld_ok && r0 + 16 <= p.M && n0 + 16 * j + 32 <= p.N;
-      store_pair_rows(p.y, p.ldy, p.M, p.N, r0, n0 + 16 * j, fr, g, full, ya, yb);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- asymmetric kernel, 32x32x32 blocks
-// 256 x 128 output tile, 8 waves of 32 rows x 128 columns, each wave's tile
+// Activation codes are unsigned with one zero-point per (row, group of 128);
+// each wave widens its A rows straight to the int8 levels u - zp (|u - zp|
+// <= 15), so the MFMA accumulates 16 * A_g exactly; every group's sum is
+// folded into fp32 with that row's scale, y += s[m, g] * acc_g in group
+// order, and the epilogue removes the factor 16 (exact) together with the
+// weight scale.
+// NW * 32 x 128 output tile (NW = 8: 256 rows, one workgroup per CU; NW = 4:
+// 128 rows, two per CU), NW waves of 32 rows x 128 columns, each wave's tile
 // as four 32x32 blocks of v_mfma_i32_32x32x32_i8.  With the weight fragment
 // first, lane (h, r) = (lane >> 5, lane & 31) accumulates activation row r
 // and weight columns 8 s + 4 h + v (s, v = 0..3) of each block, so one
@@ -498,19 +249,21 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) gemm_adirect_asym_kernel(GemmPara
 // - B: int8 weight rows in LDS as in the other kernels; quarter q's fragment
 //   of lane (h, r) is chunk 4h + q of row r, which is the same K order as
 //   A's widening.  Four stages, filled two groups at a time, so one
-//   workgroup barrier serves two groups.
+//   workgroup barrier serves two groups.  The NW * 64 threads stage 512 / (NW
+//   * 64) chunks of 16 packed bytes each per group.
 // - Order inside a group: block c's four MFMAs run back to back with the
 //   fold of block c + 1's previous group (during block 3: block 0's group g)
 //   spread over them, 8 VALU instructions after each MFMA; block c + 1's
 //   weight fragments are read during block c.  After the last group, blocks
 //   1..3 are folded once more.
-// The fold order per output (group 0, 1, ...) and the epilogue are those of
-// gemm_adirect_asym_kernel, so both kernels give identical results.
-__global__ void __launch_bounds__(512)
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
-  constexpr int BMD = 256;
+  constexpr int NT = NW * 64;
+  constexpr int NCB = 512 / NT;                     // B chunks (16 packed bytes) per thread and group
+  constexpr int BMD = NW * 32;
   constexpr int BSTAGE = 128 * LROW;                // one B stage: 128 rows x 128 int8
-  constexpr int ASTAGE = 8 * 2048;                  // one A stage: 8 waves x 32 rows x 64 packed bytes
+  constexpr int ASTAGE = NW * 2048;                 // one A stage: NW waves x 32 rows x 64 packed bytes
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * BSTAGE + 2 * ASTAGE];
   uint8_t* const sa0 = lds + 4 * BSTAGE;
   uint8_t* const sa1 = sa0 + ASTAGE;
@@ -544,8 +297,13 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
   const int a_goff = (wave * 32 + alr) * (int)ldc + 16 * ((lane & 3) ^ ((alr >> 2) & 3));
   const int a_roff0 = wave * 2048 + 64 * r + 16 * ((2 * h) ^ ((r >> 2) & 3));
   const int a_roff1 = wave * 2048 + 64 * r + 16 * ((2 * h + 1) ^ ((r >> 2) & 3));
-  const int b_off = (tid >> 2) * (int)ldc + 16 * (tid & 3);   // B staging: row tid >> 2, packed chunk tid & 3
-  const int b_lds = lds_chunk(tid >> 2, 2 * (tid & 3));
+  int b_off[NCB], b_lds[NCB];                       // B staging: chunk cb = tid + NT j -> row cb >> 2, packed chunk cb & 3
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = tid + NT * j;
+    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
+    b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
+  }
   int bfq[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) bfq[q] = lds_chunk(r, 4 * h + q);
@@ -562,17 +320,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
     z = __builtin_amdgcn_raw_buffer_load_b8(rz, arow + kc, 0, 0);
     sx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (arow + kc), 0, 0));
   };
-  auto load_b = [&](uint4& pb, int kt) {
-    pb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off + kt * 64, 0, 0));
-  };
-  auto store_b = [&](const uint4& pb, int stage) {
-    uint8_t* base = lds + stage * BSTAGE;
-    const uint32_t w[4] = {pb.x, pb.y, pb.z, pb.w};
-    uint32_t o[8];
+  auto load_b = [&](uint4* pb, int kt) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
-    *reinterpret_cast<uint4*>(base + b_lds) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(base + (b_lds ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int j = 0; j < NCB; ++j)
+      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4* pb, int stage) {
+    uint8_t* base = lds + stage * BSTAGE;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+      *reinterpret_cast<uint4*>(base + b_lds[j]) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(base + (b_lds[j] ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
   };
 
   v16i acc[4];
@@ -601,11 +364,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
     // The wait for this group's A codes (written into LDS, which the
     // compiler does not reliably track) is explicit.  Vector-memory
     // operations complete in order, and the ones issued after this group's
-    // codes, zero-point and scale are B rows of two groups (2), the next
+    // codes, zero-point and scale are B rows of two groups (2 NCB), the next
     // group's codes (2) and its zero-point and scale (2), in one order or
-    // another, so vmcnt(6) leaves the codes landed.  (A CPU test walks the
-    // compiled code's paths for this.)
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    // another, so vmcnt(2 NCB + 4) leaves the codes landed.  (A CPU test
+    // walks the compiled code's paths for this.)
+    if constexpr (NCB == 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     const uint4 pa0 = *reinterpret_cast<const uint4*>(sa + a_roff0);
     const uint4 pa1 = *reinterpret_cast<const uint4*>(sa + a_roff1);
     const uint8_t* Bs = lds + bst * BSTAGE;
@@ -654,7 +418,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
   load_zs(z[0], s[0], 0);
   load_dma(sa1, 1);
   load_zs(z[1], s[1], 1);
-  uint4 pb0, pb1;
+  uint4 pb0[NCB], pb1[NCB];
   load_b(pb0, 0);
   load_b(pb1, 1);
   store_b(pb0, 0);
@@ -838,18 +602,18 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  // asymmetric per-group activations: 256-row tiles of 8 waves with 32x32
-  // MFMA blocks from one tile per CU up (gate/up 8192 x 28672 x 8192:
-  // 2.44-2.50 ms against 2.60-2.62 ms for the 16x16x64 kernel's 256-row
-  // instance on the same boxes), else 128-row tiles of 8 waves (16 x 128
-  // each) so that small shapes still spread over the CUs
+  // asymmetric per-group activations: 256-row tiles of 8 waves from one tile
+  // per CU up (gate/up 8192 x 28672 x 8192: 2.44-2.50 ms against 2.60-2.62
+  // ms for the 16x16x64 kernel this one replaced, on the same boxes), else
+  // 128-row tiles of 4 waves, two workgroups per CU, so that small shapes
+  // still spread over the CUs (256 x 28672 x 8192: 87 against 109 us)
   const int64_t tiles_n = (p.N + BN - 1) / BN;
   const int64_t grid = ((p.M + 255) / 256) * tiles_n;
   if (grid >= 256) {
-    W4A4_LAUNCH(gemm_asym_x32_kernel, dim3((uint32_t)grid), dim3(512), 0, st, p);
+    W4A4_LAUNCH(gemm_asym_x32_kernel<8>, dim3((uint32_t)grid), dim3(512), 0, st, p);
   } else {
     const int64_t grid = ((p.M + 127) / 128) * tiles_n;
-    W4A4_LAUNCH((gemm_adirect_asym_kernel<8, 1, 2>), dim3((uint32_t)grid), dim3(512), 0, st, p);
+    W4A4_LAUNCH(gemm_asym_x32_kernel<4>, dim3((uint32_t)grid), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -5,7 +5,8 @@ LDS stage with buffer_load ... lds, two groups ahead, and reads the stage
 only after an explicit `s_waitcnt vmcnt(6)` at the top of the group's step:
 vector-memory operations complete in order, and the kernel issues six of
 them after a group's codes, zero-point and scale (B rows of two groups, the
-next group's codes and its zero-point and scale).  That only holds if the
+next group's codes and its zero-point and scale; 8 in the 4-wave instance,
+whose threads stage two B chunks each).  That only holds if the
 compiler keeps that issue order.  This test compiles gemm.hip for gfx950,
 rebuilds the kernel's control-flow graph from the assembly and walks every
 path (loop iterations, the tail steps for any group count) with the queue of
@@ -26,7 +27,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "rotation_w4a4_quantization_amd", "csrc", "gemm.hip")
-KERNEL = "_ZN4w4a420gemm_asym_x32_kernelENS_10GemmParamsE"
+# mangled name -> the explicit wait that opens a step: 2 x (B chunks per
+# thread and group) + 4
+KERNELS = {"_ZN4w4a420gemm_asym_x32_kernelILi8EEEvNS_10GemmParamsE": 6,
+           "_ZN4w4a420gemm_asym_x32_kernelILi4EEEvNS_10GemmParamsE": 8}
 LABEL = re.compile(r"^(\.LBB\w+):")
 BRANCH = re.compile(r"^\s*(s_branch|s_cbranch_\w+)\s+(\.LBB\w+)")
 END = re.compile(r"^\s*(s_endpgm|s_setpc_b64)")
@@ -43,7 +47,7 @@ def _hip_flags():
 
 
 @pytest.fixture(scope="module")
-def body(tmp_path_factory):
+def asm(tmp_path_factory):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
@@ -51,8 +55,11 @@ def body(tmp_path_factory):
     cmd = [hipcc, *_hip_flags(), "-S", "--cuda-device-only", "-I", os.path.join(ROOT, "include"), "-o", out, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    lines = open(out).read().splitlines()
-    start = next(i for i, ln in enumerate(lines) if ln.startswith(KERNEL + ":"))
+    return open(out).read().splitlines()
+
+
+def _function(lines, name):
+    start = next(i for i, ln in enumerate(lines) if ln.startswith(name + ":"))
     fn = []
     for ln in lines[start + 1:]:
         fn.append(ln)
@@ -61,7 +68,7 @@ def body(tmp_path_factory):
     return fn
 
 
-def _events(line, in_asm):
+def _events(line, in_asm, step_wait):
     """Events of one instruction: ('W', n) the explicit wait opening a step,
     ('w', n) another explicit wait, 'step' (the explicit wait that opens a group's step), 'dma', 'zs'
     (a zero-point or scale load), 'v' (other vector-memory op), 'lds_read'.
@@ -74,7 +81,7 @@ def _events(line, in_asm):
         if not in_asm:
             return []                # the compiler's own waits are not relied upon
         n = int(m.group(1))
-        return [("W", n), "step"] if n == 6 else [("w", n)]
+        return [("W", n), "step"] if n == step_wait else [("w", n)]
     if VMEM.match(line):
         if re.search(r"\blds\b", s.split(";")[0]):
             return ["dma"]
@@ -86,7 +93,7 @@ def _events(line, in_asm):
     return []
 
 
-def _cfg(fn):
+def _cfg(fn, step_wait):
     blocks, cur, evs, in_asm = [], "entry", [], False
 
     def close(succ):
@@ -112,7 +119,7 @@ def _cfg(fn):
             close([])
             cur = f"after_{len(blocks)}"
         else:
-            evs += _events(ln, in_asm)
+            evs += _events(ln, in_asm, step_wait)
     close([])
     for i, blk in enumerate(blocks):
         nxt = blocks[i + 1][0] if i + 1 < len(blocks) else None
@@ -173,8 +180,9 @@ def _walk(blocks):
     return reads, bad, steps
 
 
-def test_a_stage_reads_wait_for_their_group(body):
-    blocks = _cfg(body)
+@pytest.mark.parametrize("name", sorted(KERNELS))
+def test_a_stage_reads_wait_for_their_group(asm, name):
+    blocks = _cfg(_function(asm, name), KERNELS[name])
     reads, bad, steps = _walk(blocks)
     assert steps >= 8 and reads >= 16, (steps, reads)
     assert not bad, f"an A stage is read while its group's loads may be in flight: {bad[:3]}"
