@@ -259,13 +259,12 @@ __global__ void __launch_bounds__(kAttnThreads) kv4_attention_kernel(AttnParams 
   };
   constexpr int64_t kBatch = 16 * U;
   Batch ba, bb;
-  if (t_begin < t_end) load(ba, t_begin);
+  load(ba, t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * kBatch) {
-    const bool more = t0 + kBatch < t_end;       // uniform over the wave
-    if (more) load(bb, t0 + kBatch);
+    load(bb, t0 + kBatch);
     compute(ba, t0);
-    if (!more) break;
-    if (t0 + 2 * kBatch < t_end) load(ba, t0 + 2 * kBatch);
+    if (t0 + kBatch >= t_end) break;             // uniform over the wave
+    load(ba, t0 + 2 * kBatch);
     compute(bb, t0 + kBatch);
   }
 
