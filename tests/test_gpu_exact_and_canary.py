@@ -113,12 +113,15 @@ def test_gemm_asym_same_codes_256_row_instance(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2000, 4000, 128), (2000, 4000, 256), (2000, 4000, 384),
-                                   (1100, 7700, 640), (2048, 4096, 1280), (1100, 7700, 1408)])
+                                   (1100, 7700, 640), (2048, 4096, 1280), (1100, 7700, 1408),
+                                   (1792, 4600, 640), (1792, 4700, 640), (300, 1000, 384)])
 def test_gemm_asym_x32_group_counts_exact(M, N, K):
-    """The 256-row asymmetric kernel (32x32 MFMA blocks, groups processed in
-    pairs of a four-group loop) over 1, 2, 3, 5, 10 and 11 groups, with M and
-    N not multiples of the tile: unit scales give the oracle's integers
-    exactly."""
+    """The asymmetric kernel (32x32 MFMA blocks, groups processed in pairs of
+    a four-group loop) over 1, 2, 3, 5, 10 and 11 groups, with M and N not
+    multiples of the tile: unit scales give the oracle's integers exactly.
+    1792 x 4600 has 252 tiles of 256 rows and runs the 4-wave 128-row
+    instance, 1792 x 4700 (259 tiles) the 8-wave one; 300 x 1000 the 4-wave
+    one with a partial last tile."""
     u, zp, qw = _asym_case(M, N, K, M + N + K)
     G = K // 128
     y = host(R.w4a4_gemm(dev(O.pack_nibbles(u)), dev(np.ones((M, G), np.float32)), dev(zp.astype(np.uint8)),
