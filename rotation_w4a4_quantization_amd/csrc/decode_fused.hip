@@ -48,8 +48,37 @@ __global__ void __launch_bounds__(kFThreads) gemm_decode_fused_kernel(FusedDecod
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t nw = p.N - n0 < 16 ? p.N - n0 : 16;
 
-  // ---- 1. this workgroup's 16 weight rows: wave w takes steps w, w + 16, ...;
-  // lane (r, kg) 16 packed bytes of row n0 + r.  Issued first, consumed last.
+  // ---- 1. loads.  The activation chunks (and the sign words) are issued
+  // first and the weight rows after them: vector-memory operations complete
+  // in order, so the transform can wait for its inputs while the weight rows
+  // are still in flight.  Thread t holds quad lanes t and t + 1024 (quad =
+  // one 128-block of one row, 4 lanes of one wave).
+  const int q = tid & 3;
+  const float s0 = (q & 1) ? -1.0f : 1.0f;
+  const float s1 = (q & 2) ? -1.0f : 1.0f;
+  const float sgn = ((q ^ (q >> 1)) & 1) ? -1.0f : 1.0f;
+  const int nquad = M * nb;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.x, (short)0, (int)(M * p.ldx * 2), 0x00020000);
+  // without signs the range is empty: the loads return zeros and touch nothing
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.signs, (short)0, p.signs ? K * 2 : 0, 0x00020000);
+  uint4 xw[C][4], sd[C][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int quad = (tid + kFThreads * c) >> 2;
+    const bool ok = quad < nquad;
+    const int row = ok ? quad / nb : 0, blk = ok ? quad - row * nb : 0;
+    const int off = ok ? (row * p.ldx + blk * 128 + q * 8) * 2 : 0x7FFFFFF0;
+    const int soff = (blk * 128 + q * 8) * 2;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      xw[c][r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 64 * r4, 0));
+      sd[c][r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, soff, 64 * r4, 0));
+    }
+  }
+  // this workgroup's 16 weight rows: wave w takes steps w, w + 16, ...; lane
+  // (r, kg) 16 packed bytes of row n0 + r.  Consumed last.
   const int r = lane & 15, kg = 16 * (lane >> 4);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.wq + n0 * ldc), (short)0, (int)(nw * ldc), 0x00020000);
@@ -60,40 +89,25 @@ __global__ void __launch_bounds__(kFThreads) gemm_decode_fused_kernel(FusedDecod
     const int off = kt < nkt ? r * ldc + kg + kt * 64 : 0x7FFFFFF0;
     wb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
   }
+  // all loads issued before the transform (left alone, the scheduler sinks
+  // the second chunk's and the weights' loads below the first chunk's work)
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. rotate the M activation rows: thread t holds quad lanes t and
-  // t + 1024 (quad = one 128-block of one row, 4 lanes of one wave)
-  const int q = tid & 3;
-  const float s0 = (q & 1) ? -1.0f : 1.0f;
-  const float s1 = (q & 2) ? -1.0f : 1.0f;
-  const float sgn = ((q ^ (q >> 1)) & 1) ? -1.0f : 1.0f;
-  const int nquad = M * nb;
-  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.x, (short)0, (int)(M * p.ldx * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.signs, (short)0, p.signs ? K * 2 : 0, 0x00020000);
+  // ---- 2. rotate the M activation rows
   float v[C][32];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int quad = (tid + kFThreads * c) >> 2;
     const bool ok = quad < nquad;
-    const int row = ok ? quad / nb : 0, blk = ok ? quad - row * nb : 0;
-    const int off = ok ? (row * p.ldx + blk * 128 + q * 8) * 2 : 0x7FFFFFF0;
     uint4 w[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      w[r4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 64 * r4, 0));
-    if (p.signs) {
+    for (int r4 = 0; r4 < 4; ++r4) {
       // randomized Hadamard: flip the sign bits of the columns whose d is negative
-      const int soff = (blk * 128 + q * 8) * 2;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const uint4 d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, soff, 64 * r4, 0));
-        w[r4].x ^= d.x & 0x80008000u;
-        w[r4].y ^= d.y & 0x80008000u;
-        w[r4].z ^= d.z & 0x80008000u;
-        w[r4].w ^= d.w & 0x80008000u;
-      }
+      w[r4] = xw[c][r4];
+      w[r4].x ^= sd[c][r4].x & 0x80008000u;
+      w[r4].y ^= sd[c][r4].y & 0x80008000u;
+      w[r4].z ^= sd[c][r4].z & 0x80008000u;
+      w[r4].w ^= sd[c][r4].w & 0x80008000u;
     }
     fwht128_quad(w, v[c], s0, s1);
     float am = 0.0f;
