@@ -496,6 +496,223 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_asym_x32_kernel(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------- symmetric kernel, 32x32x32 blocks (small shapes)
+// gemm_asym_x32_kernel's structure for symmetric activations: both operands
+// widened with widen_signed, every block's accumulator carried across all K
+// (no per-group fold), and the symmetric epilogue y = (s_x[m] s_w[n]) *
+// (acc >> 8) through the same LDS transpose.  Without zero-point and scale
+// loads, the operations issued after a group's codes are B rows of two
+// groups (2 NCB) and the next group's codes (2), hence vmcnt(2 NCB + 2).  Used
+// as 128-row tiles of 4 waves where 256-row tiles would leave CUs idle but
+// 128-row ones still give at least 160 workgroups.
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(2, 2))) gemm_sym_x32_kernel(GemmParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int NCB = 512 / NT;                     // B chunks (16 packed bytes) per thread and group
+  constexpr int BMD = NW * 32;
+  constexpr int BSTAGE = 128 * LROW;                // one B stage: 128 rows x 128 int8
+  constexpr int ASTAGE = NW * 2048;                 // one A stage: NW waves x 32 rows x 64 packed bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * BSTAGE + 2 * ASTAGE];
+  uint8_t* const sa0 = lds + 4 * BSTAGE;
+  uint8_t* const sa1 = sa0 + ASTAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BMD - 1) / BMD;
+  int64_t tm, tn;
+  tile_coords_xcd(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BMD, n0 = tn * BN;
+  const int nkt = p.K / BK;
+  const int G = nkt;
+  const int64_t ldc = p.K / 2;
+
+  const int64_t a_bytes = (p.M - m0) * ldc, b_bytes = (p.N - n0) * ldc;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + m0 * ldc), (short)0, (int)(a_bytes < 0x7fffffff ? a_bytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.wq + n0 * ldc), (short)0, (int)(b_bytes < 0x7fffffff ? b_bytes : 0x7fffffff), 0x00020000);
+  // per-(row, group) zero-points and scales of this tile's rows; rows past M read as 0
+  const int64_t zs_n = (p.M - m0) * G;
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xz + m0 * G), (short)0, (int)(zs_n < 0x7fffffff ? zs_n : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xs + m0 * G), (short)0, (int)(4 * zs_n < 0x7fffffff ? 4 * zs_n : 0x7fffffff), 0x00020000);
+
+  const int h = lane >> 5, r = lane & 31;
+  const int alr = lane >> 2;                        // DMA: lane 4 R + c' carries chunk c' ^ ((R >> 2) & 3) of row R
+  const int a_goff = (wave * 32 + alr) * (int)ldc + 16 * ((lane & 3) ^ ((alr >> 2) & 3));
+  const int a_roff0 = wave * 2048 + 64 * r + 16 * ((2 * h) ^ ((r >> 2) & 3));
+  const int a_roff1 = wave * 2048 + 64 * r + 16 * ((2 * h + 1) ^ ((r >> 2) & 3));
+  int b_off[NCB], b_lds[NCB];                       // B staging: chunk cb = tid + NT j -> row cb >> 2, packed chunk cb & 3
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) {
+    const int cb = tid + NT * j;
+    b_off[j] = (cb >> 2) * (int)ldc + 16 * (cb & 3);
+    b_lds[j] = lds_chunk(cb >> 2, 2 * (cb & 3));
+  }
+  int bfq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bfq[q] = lds_chunk(r, 4 * h + q);
+  const int arow = (wave * 32 + r) * G;
+
+  auto load_dma = [&](uint8_t* sa, int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + wave * 2048 + i * 1024), 16,
+                                               a_goff + i * 16 * (int)ldc + kt * 64, 0, 0, 0);
+  };
+
+  auto load_b = [&](uint4* pb, int kt) {
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      pb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[j] + kt * 64, 0, 0));
+  };
+  auto store_b = [&](const uint4* pb, int stage) {
+    uint8_t* base = lds + stage * BSTAGE;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+      uint32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) widen_signed(w[d], o[2 * d], o[2 * d + 1]);
+      *reinterpret_cast<uint4*>(base + b_lds[j]) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(base + (b_lds[j] ^ 16)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  };
+
+  v16i acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0;
+  auto widen_q = [&](uint32_t d0, uint32_t d1) -> v4i {
+    uint32_t o[4];
+    widen_signed(d0, o[0], o[1]);
+    widen_signed(d1, o[2], o[3]);
+    return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  };
+
+  // One group: A codes from stage sa, B rows from stage bst, zero-point z,
+  // scales of this group (s_cur) and the previous one (s_prev).
+  auto step = [&](uint8_t* sa, int bst, int next_kt) {
+    // The wait for this group's A codes (written into LDS, which the
+    // compiler does not reliably track) is explicit.  Vector-memory
+    // operations complete in order, and the ones issued after this group's
+    // codes, zero-point and scale are B rows of two groups (2 NCB), the next
+    // group's codes (2) and its zero-point and scale (2), in one order or
+    // another, so vmcnt(2 NCB + 4) leaves the codes landed.  (A CPU test
+    // walks the compiled code's paths for this.)
+    if constexpr (NCB == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    const uint4 pa0 = *reinterpret_cast<const uint4*>(sa + a_roff0);
+    const uint4 pa1 = *reinterpret_cast<const uint4*>(sa + a_roff1);
+    const uint8_t* Bs = lds + bst * BSTAGE;
+    v4i a[4];
+    a[0] = widen_q(pa0.x, pa0.y);
+    a[1] = widen_q(pa0.z, pa0.w);
+    a[2] = widen_q(pa1.x, pa1.y);
+    a[3] = widen_q(pa1.z, pa1.w);
+    // the stage has been read (the widened values exist) before group
+    // next_kt's codes are requested into it
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+    load_dma(sa, next_kt);
+    __builtin_amdgcn_sched_barrier(0);
+    v4i bb[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bb[0][q] = *reinterpret_cast<const v4i*>(Bs + bfq[q]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bb[(c + 1) & 1][q] = *reinterpret_cast<const v4i*>(Bs + (c + 1) * 32 * LROW + bfq[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[c] = mfma32(bb[c & 1][q], a[q], acc[c]);
+        // pinned: left to itself the compiler gathers the folds away from
+        // the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  load_dma(sa0, 0);
+  load_dma(sa1, 1);
+  uint4 pb0[NCB], pb1[NCB];
+  load_b(pb0, 0);
+  load_b(pb1, 1);
+  store_b(pb0, 0);
+  store_b(pb1, 1);
+  lds_barrier();
+  auto pair = [&](int kt, auto J, bool two) {
+    constexpr int j = decltype(J)::value;
+    load_b(pb0, kt + 2);
+    load_b(pb1, kt + 3);
+    step(sa0, j, kt + 2);
+    if (two) step(sa1, j + 1, kt + 3);
+    store_b(pb0, (j + 2) & 3);
+    store_b(pb1, (j + 3) & 3);
+    lds_barrier();
+  };
+  int kt = 0;
+  for (; kt + 3 < nkt; kt += 4) {
+    pair(kt, IntTag<0>{}, true);
+    pair(kt + 2, IntTag<2>{}, true);
+  }
+  if (kt < nkt) pair(kt, IntTag<0>{}, kt + 1 < nkt);
+  if (kt + 2 < nkt) pair(kt + 2, IntTag<2>{}, kt + 3 < nkt);
+  // the A codes requested past the last group are still writing the stages
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                                  // the B stages become the epilogue areas
+
+  // Epilogue: each 32 x 32 block goes through a 4 KiB LDS area of the wave
+  // (rows of 128 bytes, chunk c of row R at c ^ s(R)) to full-line stores;
+  // the accumulators hold 16 x the levels' products, removed here, once,
+  // with the weight scale.
+  uint8_t* ew = lds + wave * 32 * LROW;
+  const int64_t mw = m0 + wave * 32;
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + n0), (short)0, (int)((p.N - n0) * 4 < 0x7fffffff ? (p.N - n0) * 4 : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xs + m0), (short)0, (int)((p.M - m0) * 4 < 0x7fffffff ? (p.M - m0) * 4 : 0x7fffffff), 0x00020000);
+  const int eu = lane & 7, er = lane >> 3;
+  const bool ld_ok = (p.ldy & 3) == 0;
+  float sxr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    sxr[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (wave * 32 + er + 8 * q), 0, 0));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const v4f swc = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rws, 4 * (32 * c + 4 * eu), 0, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<v4i*>(ew + r * LROW + 16 * ((2 * q + h) ^ lds_swz(r))) =
+          v4i{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = er + 8 * q;
+      const v4i av = *reinterpret_cast<const v4i*>(ew + rr * LROW + 16 * (eu ^ lds_swz(rr)));
+      v4f yv;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yv[v] = (sxr[q] * swc[v]) * (float)(av[v] >> 8);
+      const int64_t row = mw + rr;
+      const int64_t col = n0 + 32 * c + 4 * eu;
+      if (ld_ok && row < p.M && col + 4 <= p.N) {
+        __builtin_nontemporal_store(yv, reinterpret_cast<v4f*>(p.y + row * p.ldy + col));
+      } else if (row < p.M) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (col + v < p.N) p.y[row * p.ldy + col + v] = yv[v];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // ---------------------------------------------------------------- decode kernel
 // M <= 16 rows (symmetric): one workgroup per 16 output columns; the 4 waves
 // split the 128-wide K steps (wave w takes steps w, w+4, ...).  The kernel is
@@ -591,14 +808,24 @@ hipError_t launch_gemm(const GemmParams& p, int mode, hipStream_t st) {
     // A-direct kernel.  256-row tiles of 8 waves (32 x 128 each) from one
     // tile per CU up (measured faster than 16 waves of 16 x 128 at every
     // shape from 256 to 511 tiles: q_proj 32.8 vs 34.8 us, 3072 x 4096 x 4096
-    // 49 vs 63 us); fewer than one 256-row tile per CU: 64-row tiles of 4
-    // waves (M = 600: 320 workgroups instead of 96).
+    // 49 vs 63 us).
     const int64_t grid = ((p.M + 255) / 256) * ((p.N + BN - 1) / BN);
     if (grid >= 256) {
       W4A4_LAUNCH((gemm_adirect_kernel<8, 2, 4>), dim3((uint32_t)grid), dim3(512), 0, st, p);
     } else {
-      const int64_t grid = ((p.M + 63) / 64) * ((p.N + BN - 1) / BN);
-      W4A4_LAUNCH((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
+      // fewer than one 256-row tile per CU: 128-row tiles of 4 waves on
+      // 32x32 blocks from 160 of them up (1536 x 4096 x 4096: 31.2 against
+      // 40.6 us for 64-row tiles; 600 x 4096 x 14336: 65.6 against 73.8),
+      // else 64-row tiles of 4 waves (512 x 4096 x 4096, 128 tiles of 128
+      // rows: 16.9 against 19.8 us)
+      const int64_t tiles_n = (p.N + BN - 1) / BN;
+      const int64_t grid128 = ((p.M + 127) / 128) * tiles_n;
+      if (grid128 >= 160) {
+        W4A4_LAUNCH(gemm_sym_x32_kernel<4>, dim3((uint32_t)grid128), dim3(256), 0, st, p);
+      } else {
+        const int64_t grid = ((p.M + 63) / 64) * tiles_n;
+        W4A4_LAUNCH((gemm_adirect_kernel<4, 1, 2>), dim3((uint32_t)grid), dim3(256), 0, st, p);
+      }
     }
     return hipGetLastError();
   }

@@ -1,4 +1,4 @@
-"""Static check of the asymmetric 32x32-block GEMM's A-stage waits (CPU only).
+"""Static check of the 32x32-block GEMMs' A-stage waits (CPU only).
 
 gemm_asym_x32_kernel streams each group's activation codes into a per-wave
 LDS stage with buffer_load ... lds, two groups ahead, and reads the stage
@@ -29,8 +29,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "rotation_w4a4_quantization_amd", "csrc", "gemm.hip")
 # mangled name -> the explicit wait that opens a step: 2 x (B chunks per
 # thread and group) + 4
+# (the symmetric 4-wave kernel has no zero-point and scale loads: 2 x 2 + 2)
 KERNELS = {"_ZN4w4a420gemm_asym_x32_kernelILi8EEEvNS_10GemmParamsE": 6,
-           "_ZN4w4a420gemm_asym_x32_kernelILi4EEEvNS_10GemmParamsE": 8}
+           "_ZN4w4a420gemm_asym_x32_kernelILi4EEEvNS_10GemmParamsE": 8,
+           "_ZN4w4a419gemm_sym_x32_kernelILi4EEEvNS_10GemmParamsE": 6}
 LABEL = re.compile(r"^(\.LBB\w+):")
 BRANCH = re.compile(r"^\s*(s_branch|s_cbranch_\w+)\s+(\.LBB\w+)")
 END = re.compile(r"^\s*(s_endpgm|s_setpc_b64)")

@@ -58,6 +58,22 @@ def test_gemm_same_codes_sym_bitexact_large(M, N, K):
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("M,N,K", [(640, 4096, 640), (1536, 4096, 128), (1000, 3000, 1408), (700, 5000, 384),
+                                   (512, 4096, 256), (1536, 4096, 4096)])
+def test_gemm_same_codes_sym_bitexact_small_grids(M, N, K):
+    """Shapes with fewer than 256 tiles of 256 rows.  From 160 tiles of 128
+    rows the 4-wave 32x32-block kernel runs (1, 3, 5, 11 and 32 K-steps,
+    ragged M and N); 512 x 4096 (128 such tiles) takes the 64-row kernel.
+    Bit-exact against the oracle's fp32 epilogue of the exact product."""
+    qa = _codes(M + 5 * K, M, K)
+    qb = _codes(N + 7 * K, N, K)
+    rng = np.random.default_rng(M + N + K)
+    sx = (rng.random(M) * 2 + 0.01).astype(np.float32)
+    sw = (rng.random(N) * 0.01 + 1e-4).astype(np.float32)
+    y = host(R.w4a4_gemm(dev(O.pack_nibbles(qa)), dev(sx), None, dev(O.pack_nibbles(qb)), dev(sw)))
+    assert np.array_equal(y, O.epilogue_sym_f32(O.int_gemm(qa, qb), sx, sw))
+
+
 # ---------------------------------------------------------------- asymmetric, exact integers
 def _asym_case(M, N, K, seed, zp=None):
     rng = np.random.default_rng(seed)
